@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Throughput of the chunk-parallel KDA forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gva_bf16] [--no-cpu-baseline]
+
+Times K calls of kda_chunk_fwd (through the C ABI, inputs already resident in
+HBM) bracketed by device synchronisation, and prints one JSON line:
+  value         tokens per second of the whole job (Mtokens/s), tokens = B*T per call
+  roofline      the dominant kernel's achieved algorithmic bandwidth against the
+                8 TB/s HBM peak, from HIP events recorded around every stage of the
+                timed calls on the library's stream
+  cpu_baseline  the float64 oracle on the host cores, same workload
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk_kda fwd Mtokens/s at HV=32,K=V=128,T=8K; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+
+
+def algorithmic_bytes(w, inp) -> int:
+    """Every input read once and every output written once: q, k, v, g, beta, o,
+    plus the fp32 initial and final states when present."""
+    B, T, H, K = inp["q"].shape
+    HV, V = inp["v"].shape[2], inp["v"].shape[3]
+    ntok = B * T
+    qkv = inp["q"].element_size()
+    b = ntok * (2 * H * K * qkv + HV * V * qkv + HV * K * inp["g"].element_size()
+                + HV * inp["beta"].element_size() + HV * V * qkv)
+    N = inp["initial_state"].shape[0] if inp["initial_state"] is not None else len(inp["seq_lens"])
+    state = N * HV * K * V * 4
+    if inp["initial_state"] is not None:
+        b += state
+    if w.output_final_state:
+        b += state
+    return int(b)
+
+
+def algorithmic_flops(w, inp) -> int:
+    """Dense 16x16 tiles with causal sub-block skipping, per (chunk, value head):
+    NC(NC+1) BC^2 (3K + 2V) for Aqk, Akk0, W, U and Aqk V_new, 6 C K V for W S,
+    KgT V_new and Qg S, C^3/3 for the solve (BC = 16, NC = C / BC)."""
+    K, V, C = w.K, w.V, w.chunk
+    HV = inp["v"].shape[2]
+    NC, BC = C // 16, 16
+    per_chunk = NC * (NC + 1) * BC * BC * (3 * K + 2 * V) + 6 * C * K * V + C ** 3 // 3
+    chunks = sum(math.ceil(L / C) for L in inp["seq_lens"])
+    return int(per_chunk * chunks * HV)
+
+
+class Hip:
+    """The few HIP runtime calls bench.py makes itself (event timing), through the
+    runtime torch already loaded."""
+
+    def __init__(self):
+        import re
+
+        maps = open("/proc/self/maps").read()
+        paths = sorted(set(re.findall(r"(\S*libamdhip64\.so\S*)", maps)))
+        self.lib = ctypes.CDLL(paths[0])
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.lib.hipEventSynchronize(b) == 0
+        t = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return float(t.value)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_log2_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, per_launch_bytes_alg: float):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    entry = t.get("kernels", {}).get(kernel)
+    if not entry or t.get("source_digest") != source_digest():
+        return None
+    return int((entry["fetch_kib"] + entry["write_kib"]) * 1024 * t.get("copy_factor", 1.0))
+
+
+def cpu_baseline(w, inp, kw):
+    from oracle import oracle_num_threads
+    from tests.oracle_adapter import run_oracle
+
+    threads = oracle_num_threads(0)
+    t0 = time.perf_counter()
+    run_oracle(inp, kw, nthreads=threads)
+    dt = time.perf_counter() - t0
+    ntok = inp["q"].shape[0] * inp["q"].shape[1]
+    return {"value": ntok / dt / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full workload ({ntok} tokens x {inp['v'].shape[2]} value heads), float64 "
+                      f"token recurrence, {dt:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gva_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this operator is benchmarked on a single MI355X "
+              "(value heads shard across GPUs with no communication; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from gated_delta_rule_log2_amd import _abi, library
+    from gated_delta_rule_log2_amd.workloads import WORKLOADS, kernel_kwargs, make_inputs
+
+    w = WORKLOADS[args.workload]
+    kw = kernel_kwargs(w)
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    lib = library()
+    hip = Hip()
+
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    N = len(inp["seq_lens"])
+    flags = (_abi.GATE_IN_KERNEL if w.gate_in_kernel else 0) | (_abi.SAFE_GATE if w.safe_gate else 0) \
+        | (_abi.HAS_LOWER_BOUND if w.lower_bound is not None else 0) | (_abi.QK_L2NORM if w.qk_l2norm else 0) \
+        | (_abi.BETA_SIGMOID if w.beta_sigmoid else 0) | (_abi.ALLOW_NEG_EIGVAL if w.allow_neg_eigval else 0) \
+        | (_abi.OUTPUT_FINAL_STATE if w.output_final_state else 0)
+    desc = _abi.KdaFwdDesc()
+    desc.B, desc.T, desc.H, desc.HV, desc.K, desc.V = B, T, H, HV, K, V
+    desc.chunk_size = w.chunk
+    cu_host = None
+    if d["cu_seqlens"] is not None:
+        cu_host = inp["cu_seqlens"].contiguous()
+        desc.num_seqs = N
+        desc.cu_seqlens_host = ctypes.cast(cu_host.data_ptr(), ctypes.POINTER(ctypes.c_int64))
+    else:
+        desc.num_seqs = B
+    dt = {torch.float32: _abi.DTYPE_FP32, torch.bfloat16: _abi.DTYPE_BF16}
+    desc.qkv_dtype, desc.g_dtype, desc.beta_dtype = dt[d["q"].dtype], dt[d["g"].dtype], dt[d["beta"].dtype]
+    desc.scale = w.scale
+    desc.lower_bound = w.lower_bound if w.lower_bound is not None else 0.0
+    desc.flags = flags
+    nbytes = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)) == 0
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, HV, V), dtype=d["q"].dtype, device=dev)
+    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    args_ = (ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["g"]), ptr(d["beta"]), ptr(d["A_log"]),
+             ptr(d["dt_bias"]), ptr(d["initial_state"]), ptr(d["cu_seqlens"]), ptr(o), ptr(ht),
+             ptr(ws), ws.numel(), stream)
+    nst = lib.kda_chunk_fwd_stage_count()
+    names = [lib.kda_chunk_fwd_stage_name(i).decode() for i in range(nst)]
+
+    for _ in range(args.warmup):
+        rc = lib.kda_chunk_fwd(ctypes.byref(desc), *args_)
+        assert rc == 0, rc
+    torch.cuda.synchronize(dev)
+
+    events = [[hip.event() for _ in range(nst + 1)] for _ in range(args.steps)]
+    ev_arrays = [(ctypes.c_void_p * (nst + 1))(*[e.value for e in evs]) for evs in events]
+    start, end = hip.event(), hip.event()
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter()
+    hip.record(start, stream)
+    for s in range(args.steps):
+        rc = lib.kda_chunk_fwd_profiled(ctypes.byref(desc), *args_, ev_arrays[s])
+        assert rc == 0, rc
+    hip.record(end, stream)
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter() - t_wall
+    total_ms = hip.elapsed_ms(start, end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = [sum(hip.elapsed_ms(events[s][i], events[s][i + 1]) for s in range(args.steps)) / args.steps
+                for i in range(nst)]
+
+    ntok = B * T
+    value = ntok / (ms_per_step * 1e-3) / 1e6
+    alg_bytes = algorithmic_bytes(w, inp)
+    alg_flops = algorithmic_flops(w, inp)
+    dom = max(range(nst), key=lambda i: stage_ms[i])
+    t_dom = stage_ms[dom] * 1e-3
+    achieved = alg_bytes / t_dom / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(names[dom], alg_bytes),
+                "kernel": names[dom], "kernel_ms": round(stage_ms[dom], 4)}
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V, "chunk": w.chunk,
+                   "sequences": N, "safe_gate": w.safe_gate, "lower_bound": w.lower_bound,
+                   "initial_state": d["initial_state"] is not None, "final_state": w.output_final_state},
+        "roofline": roofline,
+        "path": {"algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops,
+                 "hbm_frac": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(alg_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "stages_ms": {n: round(x, 4) for n, x in zip(names, stage_ms)},
+                 "host_wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, kw)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,236 @@
+// kda_abi.cpp -- the C ABI declared in include/kda.h: argument checks, the
+// workspace layout and the launch sequence (plan -> intra -> recurrence).
+//
+// The checks follow the contract of chunk_kda described in "flash-linear-attention
+// KDA 内核工程实践…", §2.1 (chunk size, K limit, GVA divisibility, A_log
+// requirement, safe-gate lower-bound interval, allow_neg_eigval needing the beta
+// sigmoid, fp32 initial state), and the host-side validation of
+// "FlashKDA gate偏置加載路徑完整解析", §二 第2段 / §四 (fp32 A_log and dt_bias,
+// contiguous tensors, an error instead of a silent failure).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace kda {
+size_t intra_lds_bytes(int C, int K, int V, bool bf16);
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+WorkspaceLayout workspace_layout(int32_t N, int32_t total_chunks, int32_t HV, int32_t K, int32_t V,
+                                 int32_t C, size_t eb) {
+    WorkspaceLayout L{};
+    size_t off = 0;
+    L.off_chunk_off = off;
+    off = align256(off + sizeof(int32_t) * ((size_t)N + 1));
+    L.off_chunk_seq = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(total_chunks > 0 ? total_chunks : 1));
+    L.plan_bytes = off;
+    const size_t slots = (size_t)total_chunks * (size_t)HV;
+    L.off_W = off;
+    off = align256(off + eb * slots * C * K);
+    L.off_U = off;
+    off = align256(off + eb * slots * C * V);
+    L.off_KgT = off;
+    off = align256(off + eb * slots * K * C);
+    L.off_Qg = off;
+    off = align256(off + eb * slots * C * K);
+    L.off_Aqk = off;
+    off = align256(off + eb * slots * C * C);
+    L.off_d = off;
+    off = align256(off + sizeof(float) * slots * K);
+    L.total_bytes = off;
+    return L;
+}
+
+void bind_workspace(Params &p, void *ws, const WorkspaceLayout &L) {
+    unsigned char *b = static_cast<unsigned char *>(ws);
+    p.chunk_off = reinterpret_cast<int32_t *>(b + L.off_chunk_off);
+    p.chunk_seq = reinterpret_cast<int32_t *>(b + L.off_chunk_seq);
+    p.w_W = b + L.off_W;
+    p.w_U = b + L.off_U;
+    p.w_KgT = b + L.off_KgT;
+    p.w_Qg = b + L.off_Qg;
+    p.w_Aqk = b + L.off_Aqk;
+    p.w_d = reinterpret_cast<float *>(b + L.off_d);
+}
+
+// Descriptor checks shared by every entry point.  On success fills the sizes of p.
+static kda_status check_desc(const kda_fwd_desc *d, Params &p) {
+    if (!d) return KDA_ERR_NULL_POINTER;
+    if (d->B < 1 || d->T < 0 || d->H < 1 || d->HV < 1 || d->K < 1 || d->V < 1 || d->num_seqs < 0)
+        return KDA_ERR_SHAPE;
+    if ((int64_t)d->B * d->T > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (d->chunk_size != 32 && d->chunk_size != 64) return KDA_ERR_CHUNK_SIZE;
+    if (d->K > 256) return KDA_ERR_HEAD_DIM;
+    if (d->K % 32 != 0 || d->V % 32 != 0 || d->V > 256) return KDA_ERR_UNSUPPORTED;
+    if (intra_lds_bytes(d->chunk_size, d->K, d->V, d->qkv_dtype == KDA_DTYPE_BF16) > 160u * 1024u)
+        return KDA_ERR_UNSUPPORTED;  // fp32 inputs with K = V = 256 exceed one CU's LDS
+    if (d->HV % d->H != 0) return KDA_ERR_GVA;
+    const uint32_t f = d->flags;
+    if (f & ~0x7fu) return KDA_ERR_UNSUPPORTED;
+    const bool has_lb = f & KDA_HAS_LOWER_BOUND;
+    const float lb = d->lower_bound;
+    if ((f & KDA_SAFE_GATE) && (!has_lb || !(lb >= -5.f && lb < 0.f))) return KDA_ERR_LOWER_BOUND;
+    if (has_lb && !(lb < 0.f)) return KDA_ERR_LOWER_BOUND;
+    if ((f & KDA_ALLOW_NEG_EIGVAL) && !(f & KDA_BETA_SIGMOID)) return KDA_ERR_NEG_EIGVAL;
+    // sequences
+    int64_t total_chunks = 0;
+    if (d->cu_seqlens_host) {
+        if (d->B != 1 || d->num_seqs < 1) return KDA_ERR_VARLEN;
+        const int64_t *cu = d->cu_seqlens_host;
+        if (cu[0] != 0 || cu[d->num_seqs] != d->T) return KDA_ERR_VARLEN;
+        for (int n = 0; n < d->num_seqs; ++n) {
+            if (cu[n + 1] < cu[n]) return KDA_ERR_VARLEN;
+            total_chunks += (cu[n + 1] - cu[n] + d->chunk_size - 1) / d->chunk_size;
+        }
+    } else {
+        if (d->num_seqs != d->B) return KDA_ERR_SHAPE;
+        total_chunks = (int64_t)d->B * ((d->T + d->chunk_size - 1) / d->chunk_size);
+    }
+    if (total_chunks * d->HV > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
+    auto dtype_ok = [](int32_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; };
+    if (!dtype_ok(d->qkv_dtype) || !dtype_ok(d->g_dtype) || !dtype_ok(d->beta_dtype)) return KDA_ERR_DTYPE;
+
+    std::memset(&p, 0, sizeof(p));
+    p.B = d->B; p.T = d->T; p.H = d->H; p.HV = d->HV; p.K = d->K; p.V = d->V;
+    p.C = d->chunk_size;
+    p.N = d->cu_seqlens_host ? d->num_seqs : d->B;
+    p.total_chunks = (int32_t)total_chunks;
+    p.group = d->HV / d->H;
+    p.gate_mode = !(f & KDA_GATE_IN_KERNEL) ? kGatePre : (has_lb ? kGateLowerBound : kGateSoftplus);
+    p.beta_mode = !(f & KDA_BETA_SIGMOID) ? kBetaGiven : ((f & KDA_ALLOW_NEG_EIGVAL) ? kBetaTwoSigmoid : kBetaSigmoid);
+    p.qk_l2norm = (f & KDA_QK_L2NORM) ? 1 : 0;
+    p.qkv_bf16 = d->qkv_dtype == KDA_DTYPE_BF16;
+    p.g_bf16 = d->g_dtype == KDA_DTYPE_BF16;
+    p.beta_bf16 = d->beta_dtype == KDA_DTYPE_BF16;
+    p.scale = d->scale;
+    p.lower_bound_log2 = has_lb ? lb * 1.4426950408889634f : 0.f;
+    p.output_final_state = (f & KDA_OUTPUT_FINAL_STATE) ? 1 : 0;
+    return KDA_OK;
+}
+
+static kda_status to_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case KDA_ERR_CHUNK_SIZE: return "chunk_size must be 32 or 64";
+    case KDA_ERR_HEAD_DIM: return "K must be <= 256";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (K and V must be multiples of 32, V <= 256)";
+    case KDA_ERR_GVA: return "HV must be a multiple of H";
+    case KDA_ERR_MISSING_A_LOG: return "A_log is required for the in-kernel gate without a lower bound";
+    case KDA_ERR_LOWER_BOUND: return "safe_gate needs -5 <= lower_bound < 0, and a lower bound must be < 0";
+    case KDA_ERR_NEG_EIGVAL: return "allow_neg_eigval requires use_beta_sigmoid_in_kernel";
+    case KDA_ERR_VARLEN: return "cu_seqlens needs B == 1 and offsets 0 = cu[0] <= ... <= cu[N] = T";
+    case KDA_ERR_DTYPE: return "dtype must be fp32 or bf16";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+kda_status kda_chunk_fwd_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
+    Params p;
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    *bytes = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4).total_bytes;
+    return KDA_OK;
+}
+
+kda_status kda_gate_chunk_cumsum_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
+    Params p;
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    *bytes = workspace_layout(p.N, p.total_chunks, 0, p.K, p.V, p.C, 4).plan_bytes;
+    return KDA_OK;
+}
+
+static const char *const kStageNames[] = {"plan", "intra", "recurrence"};
+static const int kNumStages = 3;
+
+int kda_chunk_fwd_stage_count(void) { return kNumStages; }
+
+const char *kda_chunk_fwd_stage_name(int i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr; }
+
+kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta, const float *A_log, const float *dt_bias,
+                                  const float *initial_state, const int64_t *cu_seqlens, void *o,
+                                  float *final_state, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream, hipEvent_t *ev) {
+    Params p;
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    const bool tokens = (int64_t)d->B * d->T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_OUTPUT_FINAL_STATE) && !final_state) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
+        return KDA_ERR_MISSING_A_LOG;
+    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    const WorkspaceLayout L = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4);
+    if (!workspace || workspace_bytes < L.total_bytes) return KDA_ERR_WORKSPACE;
+
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.A_log = A_log; p.dt_bias = dt_bias; p.h0 = initial_state;
+    p.cu_seqlens = cu_seqlens;
+    p.o = o; p.ht = final_state;
+    bind_workspace(p, workspace, L);
+
+    hipError_t (*const stages[kNumStages])(const Params &, hipStream_t) = {launch_plan, launch_intra,
+                                                                            launch_recurrence};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < kNumStages && e == hipSuccess; ++i) {
+        if (ev) e = hipEventRecord(ev[i], stream);
+        if (e == hipSuccess) e = stages[i](p, stream);
+    }
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[kNumStages], stream);
+    return to_status(e);
+}
+
+kda_status kda_chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
+                         const void *g, const void *beta, const float *A_log, const float *dt_bias,
+                         const float *initial_state, const int64_t *cu_seqlens, void *o,
+                         float *final_state, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    return kda_chunk_fwd_profiled(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o,
+                                  final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_gate_chunk_cumsum(const kda_fwd_desc *d, const void *g, const float *A_log,
+                                 const float *dt_bias, const int64_t *cu_seqlens, float *g_act,
+                                 float *g_cum_log2, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    Params p;
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    const bool tokens = (int64_t)d->B * d->T > 0;
+    if (tokens && (!g || !g_cum_log2)) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
+        return KDA_ERR_MISSING_A_LOG;
+    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    const WorkspaceLayout L = workspace_layout(p.N, p.total_chunks, 0, p.K, p.V, p.C, 4);
+    if (!workspace || workspace_bytes < L.plan_bytes) return KDA_ERR_WORKSPACE;
+    p.g = g; p.A_log = A_log; p.dt_bias = dt_bias; p.cu_seqlens = cu_seqlens;
+    p.g_act = g_act; p.g_cum = g_cum_log2;
+    bind_workspace(p, workspace, L);
+    hipError_t e = launch_plan(p, stream);
+    if (e == hipSuccess) e = launch_gate_cumsum(p, stream);
+    return to_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// kda_internal.h -- launch parameters shared by the C-ABI host code and the
+// HIP kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum GateMode : int32_t { kGatePre = 0, kGateSoftplus = 1, kGateLowerBound = 2 };
+enum BetaMode : int32_t { kBetaGiven = 0, kBetaSigmoid = 1, kBetaTwoSigmoid = 2 };
+
+struct Params {
+    // sizes
+    int32_t B, T, H, HV, K, V, C;  // C = chunk size
+    int32_t N;                     // sequences
+    int32_t total_chunks;          // chunks over all sequences (each sequence starts a chunk)
+    int32_t group;                 // HV / H
+    // modes
+    int32_t gate_mode, beta_mode, qk_l2norm;
+    int32_t qkv_bf16, g_bf16, beta_bf16;
+    float scale;
+    float lower_bound_log2;        // lower_bound * log2(e): the bounded gate directly in log2 units
+    int32_t output_final_state;
+    // inputs
+    const void *q, *k, *v, *g, *beta;
+    const float *A_log, *dt_bias, *h0;
+    const int64_t *cu_seqlens;     // device offsets or nullptr (then sequence n = batch row n)
+    // outputs
+    void *o;
+    float *ht;
+    float *g_act, *g_cum;          // gate-only entry point
+    // workspace
+    int32_t *chunk_off;            // [N + 1] first global chunk of each sequence
+    int32_t *chunk_seq;            // [total_chunks] sequence of each global chunk
+    void *w_W, *w_U, *w_KgT, *w_Qg, *w_Aqk;  // per (chunk, value head) intermediates
+    float *w_d;                               // [total_chunks * HV * K] 2^(chunk gate total)
+};
+
+// Byte layout of the workspace; offsets are 256-byte aligned.
+struct WorkspaceLayout {
+    size_t off_chunk_off, off_chunk_seq, off_W, off_U, off_KgT, off_Qg, off_Aqk, off_d;
+    size_t plan_bytes, total_bytes;
+};
+
+WorkspaceLayout workspace_layout(int32_t N, int32_t total_chunks, int32_t HV, int32_t K, int32_t V,
+                                 int32_t C, size_t elem_bytes);
+void bind_workspace(Params &p, void *workspace, const WorkspaceLayout &L);
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_plan(const Params &p, hipStream_t s);
+hipError_t launch_gate_cumsum(const Params &p, hipStream_t s);
+hipError_t launch_intra(const Params &p, hipStream_t s);
+hipError_t launch_recurrence(const Params &p, hipStream_t s);
+
+}  // namespace kda
