@@ -17,7 +17,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_abi.cpp", "kda_plan_gate.hip", "kda_intra.hip", "kda_recur.hip"]
+SOURCES = [
+    "kda_abi.cpp", "kda_dispatch.hip", "kda_plan_gate.hip",
+    "kda_intra_c64_bf16.hip", "kda_intra_c64_f32.hip", "kda_intra_c32_bf16.hip", "kda_intra_c32_f32.hip",
+    "kda_recur_c64_bf16.hip", "kda_recur_c64_f32.hip", "kda_recur_c32_bf16.hip", "kda_recur_c32_f32.hip",
+]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
@@ -38,7 +42,7 @@ def _compile(src: str) -> str:
 
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 4, 16, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIBRARY + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -66,51 +66,69 @@ __device__ __forceinline__ void load8_any(const void *base, int64_t idx, int is_
 }
 
 // One wave computes, for the 16-row block `blk` of a chunk, the activated gate
-// and its inclusive cumulative sum in log2 units, in row-fragment layout:
-//   G[kk][i] = log2(e) * sum_{r' <= r} g'[r'][32*kk + 8*(l>>4) + i],  r = 16*blk + (l & 15)
-// Rows at or past the chunk's length contribute g' = 0, so they repeat the last
-// valid row's value.  Sums of earlier blocks arrive through `tot` ([nblk][K] fp32
-// in LDS), which the caller must clear-free: every block writes its own totals
-// before the __syncthreads() this function executes, and reads earlier ones after.
-// If `gact` is non-null the natural-log activated gate is stored there too.
-// All waves of the block must call this (it contains one __syncthreads()).
+// and its inclusive cumulative sum inside the block, in log2 units, in row-fragment
+// layout:  G[kk][i] = log2(e) * sum_{16*blk <= r' <= r} g'[r'][32*kk + 8*(l>>4) + i]
+// with r = 16*blk + (l & 15).  Rows at or past the chunk's length contribute
+// g' = 0, so they repeat the last valid row's value.  gact receives g' itself.
 template <int NKK>
-__device__ __forceinline__ void gate_cumsum_block(const Params &p, const ChunkInfo &ci, int hv, int blk,
-                                                  int nkk, float (&G)[NKK][8], float *tot,
-                                                  float (&gact)[NKK][8]) {
+__device__ __forceinline__ void gate_scan_block(const Params &p, const ChunkInfo &ci, int hv, int blk, int nkk,
+                                                float (&G)[NKK][8], float (&gact)[NKK][8]) {
     const int l = lane_id();
     const int r = 16 * blk + (l & 15);
     const int cg = l >> 4;
     const bool valid = r < ci.L;
     const int K = p.K;
-    const float a = (p.gate_mode == kGatePre) ? 1.f : (p.A_log ? expf(p.A_log[hv]) : 1.f);
-    const float lb = p.lower_bound_log2 / kLog2e;
     const int64_t row = ((ci.tok0 + r) * p.HV + hv) * (int64_t)K;
+    // raw gate rows (one dtype branch for the whole block)
+    if (valid) {
+        if (p.g_bf16) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        if (kk < nkk) {
-            const int d0 = 32 * kk + 8 * cg;
-            float x[8];
-            if (valid) load8_any(p.g, row + d0, p.g_bf16, x);
+            for (int kk = 0; kk < NKK; ++kk)
+                if (kk < nkk) load8(static_cast<const uint16_t *>(p.g) + row + 32 * kk + 8 * cg, G[kk]);
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float dtb = (p.dt_bias && p.gate_mode != kGatePre) ? p.dt_bias[(int64_t)hv * K + d0 + i] : 0.f;
-                const float gn = valid ? gate_natural(p.gate_mode, x[i], dtb, a, lb) : 0.f;
-                gact[kk][i] = gn;
-                G[kk][i] = row_scan16(gn * kLog2e);
+            for (int kk = 0; kk < NKK; ++kk)
+                if (kk < nkk) load8(static_cast<const float *>(p.g) + row + 32 * kk + 8 * cg, G[kk]);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) G[kk][i] = 0.f;
+    }
+    if (p.gate_mode != kGatePre) {
+        const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
+        const float lb = p.lower_bound_log2 / kLog2e;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            if (kk < nkk) {
+                float dtb[8];
+                if (p.dt_bias) load8(p.dt_bias + (int64_t)hv * K + 32 * kk + 8 * cg, dtb);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dtb[i] = 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) G[kk][i] = valid ? gate_natural(p.gate_mode, G[kk][i], dtb[i], a, lb) : 0.f;
             }
         }
     }
-    // block totals (row 15 of this block) -> LDS
-    if ((l & 15) == 15) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            if (kk < nkk) {
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (kk < nkk) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) tot[blk * K + 32 * kk + 8 * cg + i] = G[kk][i];
+            for (int i = 0; i < 8; ++i) {
+                gact[kk][i] = G[kk][i];
+                G[kk][i] = row_scan16(G[kk][i] * kLog2e);
             }
+        }
     }
-    __syncthreads();
+}
+
+// Adds the totals of the earlier blocks (from `tot`, [nblk][K] fp32) to a block scan.
+template <int NKK>
+__device__ __forceinline__ void gate_add_prefix(const float *tot, int K, int blk, int nkk, float (&G)[NKK][8]) {
+    const int cg = lane_id() >> 4;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
         if (kk < nkk) {
@@ -121,6 +139,29 @@ __device__ __forceinline__ void gate_cumsum_block(const Params &p, const ChunkIn
                 G[kk][i] += pre;
             }
         }
+}
+
+// Full chunk-local cumsum for the block: block scan, block totals through `tot`
+// (LDS [nblk][K] fp32), one __syncthreads() (every wave of the workgroup must
+// call this), then the earlier blocks' totals added.
+template <int NKK>
+__device__ __forceinline__ void gate_cumsum_block(const Params &p, const ChunkInfo &ci, int hv, int blk,
+                                                  int nkk, float (&G)[NKK][8], float *tot,
+                                                  float (&gact)[NKK][8]) {
+    const int l = lane_id();
+    const int cg = l >> 4;
+    const int K = p.K;
+    gate_scan_block<NKK>(p, ci, hv, blk, nkk, G, gact);
+    if ((l & 15) == 15) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            if (kk < nkk) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) tot[blk * K + 32 * kk + 8 * cg + i] = G[kk][i];
+            }
+    }
+    __syncthreads();
+    gate_add_prefix<NKK>(tot, K, blk, nkk, G);
 }
 
 }  // namespace kda

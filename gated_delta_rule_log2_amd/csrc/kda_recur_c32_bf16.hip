@@ -1,0 +1,7 @@
+// Recurrence kernels for chunk size 32, bf16 storage (one translation unit per
+// combination so the exact-K instantiations compile in parallel).
+#include "kda_recur.h"
+
+namespace kda {
+hipError_t launch_recur_c32_bf16(const Params &p, hipStream_t s) { return launch_recur_ct<32, uint16_t>(p, s); }
+}  // namespace kda
