@@ -8,7 +8,7 @@
 //   Akk0[i][j] = b_i sum_d k^_id k^_jd 2^(G_id - G_jd)      (j <  i)
 //   A = (I + Akk0)^-1,  W = A (b * 2^G * k^),  U = A (b * v)
 //   Qg = 2^G * q^,  KgT = (2^(G_last - G) * k^)^T,  d = 2^G_last
-// which the recurrence kernel consumes (U is stored transposed, U^T [V][C]).
+// which the recurrence kernel consumes, stored in the fragment-major layouts below.
 //
 // Exponent handling ("flash-linear-attention KDA 内核工程实践…", §3.1 and §3.2):
 //   - sub-chunk pairs (p > s) factor 2^(G_i - G_j) as 2^(G_i - G_n) * 2^(G_n - G_j)
@@ -81,8 +81,19 @@ __device__ __forceinline__ f32x4 mma16_f32_lds(f32x4 acc, const float *X, int ld
     return acc;
 }
 
-template <typename T>
-__device__ __forceinline__ void load8_lds(const T *p, float (&o)[8]) { load8(p, o); }
+// Fragment-major layouts of the per-chunk intermediates, in exactly the order the
+// recurrence kernel's lanes load them (each wave-wide load is one contiguous 1 KB
+// (bf16) run instead of 16 partial cache lines):
+//   row fragments (W, Qg [C][K]; Aqk [C][C]; KgT [K][C]): element (row, col) at
+//     ((row/16 * (ncols/32) + col/32) * 64 + row%16 + 16 * ((col%32)/8)) * 8 + col%8
+//   U in accumulator quads: element U[m][v] at
+//     ((v/16 * (C/16) + m/16) * 64 + v%16 + 16 * ((m%16)/4)) * 4 + m%4
+__host__ __device__ __forceinline__ size_t frag_off(int row, int col, int ncols) {
+    return ((size_t)((row >> 4) * (ncols >> 5) + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
+}
+__host__ __device__ __forceinline__ size_t quad_off(int m, int v, int C) {
+    return ((size_t)((v >> 4) * (C >> 4) + (m >> 4)) * 64 + (v & 15) + 16 * ((m & 15) >> 2)) * 4 + (m & 3);
+}
 
 template <int C, typename T, int NKK>
 __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
@@ -243,7 +254,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
             load8(SC + sc_en(w) * K + d0, en);
 #pragma unroll
             for (int i = 0; i < 8; ++i) qg8[i] = QR[kk][i] * en[i];
-            store8(Qgg + (size_t)r * K + d0, qg8);
+            store8(Qgg + frag_off(r, d0, K), qg8);
         }
     }
 
@@ -305,7 +316,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
             ak[jj] = (s < w || (s == w && jl < lr)) ? b_r * vk[jj] : 0.f;
         }
         if (!(s == w && diag_fallback)) {
-            store4(Aqkg + (size_t)r * C + 16 * s + 4 * cg, aq[0], aq[1], aq[2], aq[3]);
+            store4(Aqkg + frag_off(r, 16 * s + 4 * cg, C), aq[0], aq[1], aq[2], aq[3]);
             store4(Akk + r * LDA + 16 * s + 4 * cg, ak[0], ak[1], ak[2], ak[3]);
         }
     }
@@ -346,7 +357,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
             sq = sum_col_groups(sq);
             sk = sum_col_groups(sk);
             if (cg == 0) {
-                Aqkg[(size_t)r * C + 16 * w + jr] = Store<T>::to(lr >= jr ? sq : 0.f);
+                Aqkg[frag_off(r, 16 * w + jr, C)] = Store<T>::to(lr >= jr ? sq : 0.f);
                 Akk[r * LDA + 16 * w + jr] = lr > jr ? b_r * sk : 0.f;
             }
         }
@@ -371,7 +382,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
         float v8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v8[i] = Store<T>::from(KCs[(8 * mo + i) * LDK + d]) * kg;
-        store8(KgTg + (size_t)d * C + 8 * mo, v8);
+        store8(KgTg + frag_off(d, 8 * mo, C), v8);
     }
 
     // ---- step 7: A = (I + Akk0)^-1, fp32 ----
@@ -451,7 +462,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
                     acc = mma32<F32>(acc, bx, am[ms]);
                 }
             }
-            store4(Wg + (size_t)r * K + 16 * dt + 4 * cg, acc[0], acc[1], acc[2], acc[3]);
+            store4(Wg + frag_off(r, 16 * dt + 4 * cg, K), acc[0], acc[1], acc[2], acc[3]);
         }
         for (int vt = 0; vt < V / 16; ++vt) {
             f32x4 acc = zero4();
@@ -463,7 +474,7 @@ __global__ void __launch_bounds__(C / 16 * 64) intra_kernel(Params p) {
                     acc = mma32<F32>(acc, am[ms], bx);
                 }
             }
-            store4(UTg + (size_t)(16 * vt + lr) * C + 16 * w + 4 * cg, acc[0], acc[1], acc[2], acc[3]);
+            store4(UTg + quad_off(16 * w + 4 * cg, 16 * vt + lr, C), acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
