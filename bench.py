@@ -112,7 +112,7 @@ def load_traffic(kernel: str, per_launch_bytes_alg: float):
     entry = t.get("kernels", {}).get(kernel)
     if not entry or t.get("source_digest") != source_digest():
         return None
-    return int((entry["fetch_kib"] + entry["write_kib"]) * 1024 * t.get("copy_factor", 1.0))
+    return int(entry["fetch_kib"] * 1024 * t["copy_factor_fetch"] + entry["write_kib"] * 1024 * t["copy_factor_write"])
 
 
 def cpu_baseline(w, inp, kw):
@@ -136,6 +136,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gva_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (5 times), the known-size "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +148,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}), flush=True)
+        return 0
 
     from gated_delta_rule_log2_amd import _abi, library
     from gated_delta_rule_log2_amd.workloads import WORKLOADS, kernel_kwargs, make_inputs
