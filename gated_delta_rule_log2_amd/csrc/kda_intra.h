@@ -88,11 +88,22 @@ __device__ __forceinline__ f32x4 mma16_f32_lds(f32x4 acc, const float *X, int ld
 //     ((row/16 * (ncols/32) + col/32) * 64 + row%16 + 16 * ((col%32)/8)) * 8 + col%8
 //   U in accumulator quads: element U[m][v] at
 //     ((v/16 * (C/16) + m/16) * 64 + v%16 + 16 * ((m%16)/4)) * 4 + m%4
+//   permuted row fragments: as row fragments, but the 8 contraction indices of lane
+//     group g inside a 32-column block are {4g..4g+3} and {16+4g..16+4g+3}, i.e.
+//     element (row, col) at
+//     ((row/16 * (ncols/32) + col/32) * 64 + row%16 + 16 * ((col%16)/4)) * 8 + 4 * ((col%32)/16) + col%4
+//     With this order the accumulator layout of a 16x16 product (lane group g holds
+//     rows 4g..4g+3) is, two tiles at a time, already the contraction-operand layout
+//     of the next product, so results feed matrix cores without a lane exchange.
 __host__ __device__ __forceinline__ size_t frag_off(int row, int col, int ncols) {
     return ((size_t)((row >> 4) * (ncols >> 5) + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
 }
 __host__ __device__ __forceinline__ size_t quad_off(int m, int v, int C) {
     return ((size_t)((v >> 4) * (C >> 4) + (m >> 4)) * 64 + (v & 15) + 16 * ((m & 15) >> 2)) * 4 + (m & 3);
+}
+__host__ __device__ __forceinline__ size_t pfrag_off(int row, int col, int ncols) {
+    return ((size_t)((row >> 4) * (ncols >> 5) + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 15) >> 2)) * 8 +
+           4 * ((col & 31) >> 4) + (col & 3);
 }
 
 template <int C, typename T, int NKK>

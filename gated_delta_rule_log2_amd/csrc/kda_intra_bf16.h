@@ -106,9 +106,15 @@ struct IntraBf16Lds {
 #define KDA_INTRA_OCC
 #endif
 
+// Key widths up to 128 store W, Qg, Aqk and KgT as permuted row fragments (the
+// layout of the register-resident recurrence); wider keys keep plain row fragments.
+template <int K>
+__host__ __device__ constexpr bool permuted_layout() { return K <= 128; }
+
 template <int C, int NKK>
 __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(Params p) {
     constexpr int NB = C / 16, K = 32 * NKK;
+    constexpr bool PERM = permuted_layout<K>();
     using L_ = IntraBf16Lds<C, K>;
     constexpr int LDA = L_::LDA;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -132,7 +138,9 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     auto pair_of = [](int wb, int sb) { return wb * (wb - 1) / 2 + sb; };
 
     const int hv = blockIdx.x % p.HV;
-    const int gc = blockIdx.x / p.HV;
+    // chunks are taken last-to-first, so the first chunks the recurrence reads are the
+    // most recently written ones (still in the memory-side cache)
+    const int gc = p.total_chunks - 1 - (int)(blockIdx.x / p.HV);
     const int h = hv / p.group;
     const ChunkInfo ci = chunk_info(p, gc);
     const int w = threadIdx.x >> 6;
@@ -342,7 +350,13 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             accQd = mma32_bf16(accQd, b1p, pack8(a1));
             accKd = mma32_bf16(accKd, b1p, pack8(a2));
         }
-        *reinterpret_cast<uint4 *>(Qgg + frag_off(r, d0, K)) = pack8(qg);
+        if constexpr (PERM) {
+            *reinterpret_cast<uint2 *>(Qgg + pfrag_off(r, d0, K)) = make_uint2(pack2(qg[0], qg[1]), pack2(qg[2], qg[3]));
+            *reinterpret_cast<uint2 *>(Qgg + pfrag_off(r, d0 + 4, K)) =
+                make_uint2(pack2(qg[4], qg[5]), pack2(qg[6], qg[7]));
+        } else {
+            *reinterpret_cast<uint4 *>(Qgg + frag_off(r, d0, K)) = pack8(qg);
+        }
         if (w < NB - 1) OPS[(w * NKK + kk) * 64 + l] = pack8(kc);
         // KgT: transpose the 16x32 block on the matrix cores, stage [d][m] in LDS
         const uint4 ktp = pack8(kt);
@@ -380,8 +394,16 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     for (int u = threadIdx.x; u < K * C / 8; u += blockDim.x) {
         const int tile = u >> 6, within = u & 63;
         const int d = 16 * (tile / (C / 32)) + (within & 15);
-        const int m0 = 32 * (tile % (C / 32)) + 8 * (within >> 4);
-        *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(KST + swz<C>(d, m0));
+        if constexpr (PERM) {
+            // lane group g of a unit holds columns 4g..4g+3 and 16+4g..16+4g+3 of its 32-column block
+            const int m0 = 32 * (tile % (C / 32)) + 4 * (within >> 4);
+            const uint2 a = *reinterpret_cast<const uint2 *>(KST + swz<C>(d, m0));
+            const uint2 b = *reinterpret_cast<const uint2 *>(KST + swz<C>(d, m0 + 16));
+            *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = make_uint4(a.x, a.y, b.x, b.y);
+        } else {
+            const int m0 = 32 * (tile % (C / 32)) + 8 * (within >> 4);
+            *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(KST + swz<C>(d, m0));
+        }
     }
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -393,7 +415,7 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             aq[jj] = (s < w || (s == w && jl <= lr)) ? vq[jj] : 0.f;
             ak[jj] = (s < w || (s == w && jl < lr)) ? b_r * vk[jj] : 0.f;
         }
-        *reinterpret_cast<uint2 *>(Aqkg + frag_off(r, 16 * s + 4 * cg, C)) =
+        *reinterpret_cast<uint2 *>(Aqkg + (PERM ? pfrag_off(r, 16 * s + 4 * cg, C) : frag_off(r, 16 * s + 4 * cg, C))) =
             make_uint2(pack2(aq[0], aq[1]), pack2(aq[2], aq[3]));
         store4(Akk + r * LDA + 16 * s + 4 * cg, ak[0], ak[1], ak[2], ak[3]);
     }
@@ -492,7 +514,7 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             if (ms < nms)
                 acc = mma32_bf16(acc, *reinterpret_cast<const uint4 *>(XT + swz<C>(16 * dt + lr, 32 * ms + 8 * cg)),
                                  am[ms]);
-        *reinterpret_cast<uint2 *>(Wg + frag_off(r, 16 * dt + 4 * cg, K)) =
+        *reinterpret_cast<uint2 *>(Wg + (PERM ? pfrag_off(r, 16 * dt + 4 * cg, K) : frag_off(r, 16 * dt + 4 * cg, K))) =
             make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
     for (int vt = 0; vt < V / 16; ++vt) {

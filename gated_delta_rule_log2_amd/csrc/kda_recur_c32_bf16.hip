@@ -1,7 +1,11 @@
-// Recurrence kernels for chunk size 32, bf16 storage (one translation unit per
-// combination so the exact-K instantiations compile in parallel).
-#include "kda_recur.h"
+// Recurrence kernels for chunk size 32, bf16 intermediates: the register-resident
+// chain for key widths up to 128 (the intra kernel writes permuted fragments there),
+// the LDS-exchange kernel above that.
+#include "kda_recur_reg.h"
 
 namespace kda {
-hipError_t launch_recur_c32_bf16(const Params &p, hipStream_t s) { return launch_recur_ct<32, uint16_t>(p, s); }
+hipError_t launch_recur_c32_bf16(const Params &p, hipStream_t s) {
+    if (p.K <= 128) return launch_recur_reg<32>(p, s);
+    return launch_recur_ct<32, uint16_t>(p, s);
+}
 }  // namespace kda

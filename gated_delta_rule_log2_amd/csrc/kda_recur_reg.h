@@ -1,0 +1,297 @@
+// kda_recur_reg.h -- inter-chunk state recurrence and chunk output of the KDA
+// forward for bf16 intermediates and key width <= 128, with the state chain kept
+// in registers and no cross-wave exchange on it.
+//
+// "Reading Notes: Implementation Notes for KDA in FLA", forward steps 4 and 5, with
+// the state stored [K][V] and its decay read as Diag(2^G_last):
+//   V_new = U - W S,   O = Qg S + Aqk V_new (S before the update),
+//   S <- Diag(d) S + KgT V_new,   d = 2^G_last
+//
+// One workgroup of 4 waves per (sequence, value head, 32-column slice of V):
+//   waves 0, 1  state waves: wave j owns columns 16j..16j+15 of the slice and all K
+//               rows of S (fp32 accumulators).  W, KgT, Qg and Aqk are stored as
+//               permuted row fragments (see pfrag_off), so S and V_new in accumulator
+//               layout are, converted to bf16 in place, the contraction operands of
+//               the next products: the whole chain W S -> V_new -> KgT V_new -> S runs
+//               inside one wave.
+//   wave 2      output wave: one step behind, O = Qg S + Aqk V_new for both column
+//               halves from the S and V_new the state waves hand over through LDS,
+//               with Qg and Aqk prefetched a step ahead into its own registers; O is
+//               staged in LDS and written as 16-byte row segments.
+//   wave 3      loader: streams each step's W, KgT, U slice and d into a 3-slot LDS
+//               ring with direct global->LDS loads, two steps ahead of the state waves.
+// One barrier per step orders the ring, the hand-over buffers and the waves.
+//
+// Placement: workgroups are dealt to the 8 XCDs round-robin by index; the index is
+// arranged so every V slice of one (sequence, head) runs on the same XCD and shares
+// that XCD's L2 copy of the head's operands.
+#pragma once
+
+#include "kda_intra_bf16.h"
+#include "kda_recur.h"
+
+namespace kda {
+
+template <int C, int K>
+struct RegRecur {
+    static constexpr int NKK = K / 32, NMT = C / 16, NMS = C / 32, NT = K / 16;
+    static constexpr int NS = 3;  // ring slots
+    // one ring slot (bytes): W [NMT][NKK] and KgT [NT][NMS] fragment units of 1 KB, U for
+    // the slice's two 16-column tiles ([2][NMT] quad units of 512 B), d [K] fp32
+    static constexpr size_t kW = 0, kKgT = kW + (size_t)C * K * 2, kU = kKgT + (size_t)K * C * 2;
+    static constexpr size_t kD = kU + (size_t)C * 32 * 2, kSlot = kD + (size_t)K * 4;
+    // hand-over buffers [2][2 state waves]: S as [NKK] operand units, V_new as [NMS] units
+    static constexpr size_t kExWave = (size_t)(NKK + NMS) * 1024;
+    static constexpr size_t kEx = NS * kSlot, kOs = kEx + 4 * kExWave;
+    static constexpr int LDO = kBV + 8;  // output tile row stride (bf16)
+    static constexpr size_t kBytes = kOs + (size_t)C * LDO * 2;
+    // loader instructions per step: 1 KB units of W, KgT and U, then d as 16 bytes on
+    // each of the first K/4 lanes
+    static constexpr int NLW = C * K * 2 / 1024, NLU = C * 32 * 2 / 1024;
+    static constexpr int NLOAD = 2 * NLW + NLU + 1;
+    static_assert(K / 4 <= 64, "d in one load");
+    static_assert(NLOAD <= 63, "loader wait count");
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave
+// are outstanding (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+__device__ __forceinline__ void lds_dma16(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+template <int C, int NKK>
+__global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
+    constexpr int K = 32 * NKK;
+    using R = RegRecur<C, K>;
+    constexpr int NMT = R::NMT, NMS = R::NMS, NT = R::NT, NS = R::NS;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int V = p.V;
+
+    // XCD-aware decode: workgroup b runs on XCD b % 8; unit u = (n, hv) lives on XCD u % 8
+    const int nvt = V / kBV;
+    const int xcd = blockIdx.x % kXCD, pos = blockIdx.x / kXCD;
+    const int u = (pos / nvt) * kXCD + xcd;
+    if (u >= p.N * p.HV) return;
+    const int n = u / p.HV, hv = u % p.HV;
+    const int v0 = kBV * (pos % nvt);
+    const int wid = threadIdx.x >> 6, l = lane_id(), lr = l & 15, cg = l >> 4;
+
+    const int c0 = p.chunk_off[n], c1 = p.chunk_off[n + 1];
+    const int nsteps = c1 - c0;
+    const int64_t sb = seq_begin(p, n);
+    const int64_t se = p.cu_seqlens ? p.cu_seqlens[n + 1] : sb + p.T;
+    auto slot_of = [&](int k) { return (size_t)(c0 + k) * p.HV + hv; };
+    unsigned char *ring = lds;
+    auto ex_s = [&](int e, int j) { return reinterpret_cast<uint4 *>(lds + R::kEx + (size_t)(2 * e + j) * R::kExWave); };
+    auto ex_v = [&](int e, int j) { return ex_s(e, j) + NKK * 64; };
+    uint16_t *OS = reinterpret_cast<uint16_t *>(lds + R::kOs);
+
+    if (wid < 2) {
+        // ------------------------------------------------------------ state wave j
+        const int j = wid;
+        const int col = v0 + 16 * j + lr;
+        const size_t sbase = ((size_t)n * p.HV + hv) * K * V;
+        f32x4 S[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            S[t] = zero4();
+            if (p.h0) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) S[t][jj] = p.h0[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col];
+            }
+        }
+        for (int k = 0; k <= nsteps; ++k) {
+            __syncthreads();
+            if (k == nsteps) break;
+            const unsigned char *sl = ring + (size_t)(k % NS) * R::kSlot;
+            const uint4 *Wr = reinterpret_cast<const uint4 *>(sl + R::kW);
+            const uint4 *Kr = reinterpret_cast<const uint4 *>(sl + R::kKgT);
+            const uint2 *Ur = reinterpret_cast<const uint2 *>(sl + R::kU);
+            const float4 *Dr = reinterpret_cast<const float4 *>(sl + R::kD);
+            uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
+            // S in bf16 as the contraction operand (permuted order), handed to the output wave
+            uint4 Sb[NKK];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                Sb[kk] = make_uint4(pack2(S[2 * kk][0], S[2 * kk][1]), pack2(S[2 * kk][2], S[2 * kk][3]),
+                                    pack2(S[2 * kk + 1][0], S[2 * kk + 1][1]),
+                                    pack2(S[2 * kk + 1][2], S[2 * kk + 1][3]));
+                xs[kk * 64 + l] = Sb[kk];
+            }
+            // V_new = U - W S  (accumulator layout: rows 16mt+4cg+jj, column lr)
+            f32x4 Vn[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) acc = mma32_bf16(acc, Wr[(mt * NKK + kk) * 64 + l], Sb[kk]);
+                const uint2 uq = Ur[(j * NMT + mt) * 64 + l];
+                Vn[mt][0] = __uint_as_float(uq.x << 16) - acc[0];
+                Vn[mt][1] = __uint_as_float(uq.x & 0xffff0000u) - acc[1];
+                Vn[mt][2] = __uint_as_float(uq.y << 16) - acc[2];
+                Vn[mt][3] = __uint_as_float(uq.y & 0xffff0000u) - acc[3];
+            }
+            uint4 Vb[NMS];
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) {
+                Vb[ms] = make_uint4(pack2(Vn[2 * ms][0], Vn[2 * ms][1]), pack2(Vn[2 * ms][2], Vn[2 * ms][3]),
+                                    pack2(Vn[2 * ms + 1][0], Vn[2 * ms + 1][1]),
+                                    pack2(Vn[2 * ms + 1][2], Vn[2 * ms + 1][3]));
+                xv[ms * 64 + l] = Vb[ms];
+            }
+            // S <- Diag(d) S + KgT V_new
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float4 dd = Dr[4 * t + cg];
+                f32x4 acc = S[t];
+                acc[0] *= dd.x;
+                acc[1] *= dd.y;
+                acc[2] *= dd.z;
+                acc[3] *= dd.w;
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) acc = mma32_bf16(acc, Kr[(t * NMS + ms) * 64 + l], Vb[ms]);
+                S[t] = acc;
+            }
+        }
+        if (p.output_final_state) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) p.ht[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col] = S[t][jj];
+        }
+    } else if (wid == 2) {
+        // ------------------------------------------------------------ output wave
+        // Qg / Aqk fragments for one step: Qg [NMT][NKK], Aqk [NMT][NMS] (only the
+        // blocks at or left of the diagonal are read)
+        struct QA {
+            uint4 q[NMT][NKK];
+            uint4 a[NMT][NMS];
+        };
+        auto load_qa = [&](QA &x, int k) {
+            const size_t sl = slot_of(k);
+            const uint4 *Qr = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w_Qg) + sl * C * K);
+            const uint4 *Ar = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w_Aqk) + sl * C * C);
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) x.q[mt][kk] = Qr[(mt * NKK + kk) * 64 + l];
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms)
+                    if (32 * ms <= 16 * mt + 15) x.a[mt][ms] = Ar[(mt * NMS + ms) * 64 + l];
+            }
+        };
+        auto out_step = [&](const QA &x, int k) {
+            // output of step k from hand-over buffer k & 1
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
+                uint4 Sb[NKK], Vb[NMS];
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) Sb[kk] = xs[kk * 64 + l];
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) Vb[ms] = xv[ms * 64 + l];
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) acc = mma32_bf16(acc, Sb[kk], x.q[mt][kk]);
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms)
+                        if (32 * ms <= 16 * mt + 15) acc = mma32_bf16(acc, Vb[ms], x.a[mt][ms]);
+                    // lane: row 16mt+lr, columns 16j+4cg..+3
+                    *reinterpret_cast<uint2 *>(OS + (16 * mt + lr) * R::LDO + 16 * j + 4 * cg) =
+                        make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+                }
+            }
+            const int64_t tok0 = sb + (int64_t)k * C;
+            const int L = (int)((se - tok0) < C ? (se - tok0) : C);
+#pragma unroll
+            for (int it = 0; it < C / 16; ++it) {
+                const int m = 16 * it + (l >> 2), c8 = 8 * (l & 3);
+                if (m < L)
+                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.o) + ((tok0 + m) * p.HV + hv) * (int64_t)V +
+                                               v0 + c8) = *reinterpret_cast<const uint4 *>(OS + m * R::LDO + c8);
+            }
+        };
+        QA qa[2];
+        // iteration k: prefetch step k's operands, barrier, output of step k - 1
+        int k = 0;
+        for (; k + 1 <= nsteps; k += 2) {
+            load_qa(qa[0], k);
+            __syncthreads();
+            if (k >= 1) out_step(qa[1], k - 1);
+            if (k + 1 < nsteps) load_qa(qa[1], k + 1);
+            __syncthreads();
+            out_step(qa[0], k);
+        }
+        if (k <= nsteps) {  // k == nsteps: the last barrier and the final output
+            __syncthreads();
+            if (k >= 1) out_step(qa[1], k - 1);
+        }
+    } else {
+        // ------------------------------------------------------------ loader wave
+        auto issue = [&](int k) {
+            const size_t sl = slot_of(k);
+            unsigned char *dst = ring + (size_t)(k % NS) * R::kSlot;
+            const unsigned char *gW = reinterpret_cast<const unsigned char *>(p.w_W) + sl * C * K * 2;
+            const unsigned char *gK = reinterpret_cast<const unsigned char *>(p.w_KgT) + sl * K * C * 2;
+            const unsigned char *gU = reinterpret_cast<const unsigned char *>(p.w_U) +
+                                      (sl * (size_t)V * C + quad_off(0, v0, C)) * 2;
+            const unsigned char *gD = reinterpret_cast<const unsigned char *>(p.w_d + sl * K);
+#pragma unroll
+            for (int i = 0; i < R::NLW; ++i) lds_dma16(gW + i * 1024 + l * 16, dst + R::kW + i * 1024);
+#pragma unroll
+            for (int i = 0; i < R::NLW; ++i) lds_dma16(gK + i * 1024 + l * 16, dst + R::kKgT + i * 1024);
+#pragma unroll
+            for (int i = 0; i < R::NLU; ++i) lds_dma16(gU + i * 1024 + l * 16, dst + R::kU + i * 1024);
+            if (l < K / 4) lds_dma16(gD + l * 16, dst + R::kD);
+        };
+        if (nsteps > 0) issue(0);
+        if (nsteps > 1) {
+            issue(1);
+            wait_vmcnt<R::NLOAD>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        for (int k = 0; k <= nsteps; ++k) {
+            __builtin_amdgcn_s_barrier();
+            if (k + 2 < nsteps) {
+                issue(k + 2);
+                wait_vmcnt<R::NLOAD>();  // step k + 1 has landed
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+    }
+}
+
+template <int C>
+hipError_t launch_recur_reg(const Params &p, hipStream_t s) {
+    const int units = p.N * p.HV;
+    const int per_xcd = (units + kXCD - 1) / kXCD;
+    const dim3 grid((unsigned)(per_xcd * kXCD * (p.V / kBV)));
+    hipError_t e = hipSuccess;
+    auto go = [&](auto kern, size_t lds) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+        if (e != hipSuccess) return;
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+        e = hipGetLastError();
+    };
+    switch (p.K / 32) {
+    case 1: go(recur_reg_kernel<C, 1>, RegRecur<C, 32>::kBytes); break;
+    case 2: go(recur_reg_kernel<C, 2>, RegRecur<C, 64>::kBytes); break;
+    case 3: go(recur_reg_kernel<C, 3>, RegRecur<C, 96>::kBytes); break;
+    case 4: go(recur_reg_kernel<C, 4>, RegRecur<C, 128>::kBytes); break;
+    default: return hipErrorInvalidValue;
+    }
+    return e;
+}
+
+}  // namespace kda
