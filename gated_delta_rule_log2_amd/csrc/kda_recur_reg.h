@@ -7,18 +7,20 @@
 //   V_new = U - W S,   O = Qg S + Aqk V_new (S before the update),
 //   S <- Diag(d) S + KgT V_new,   d = 2^G_last
 //
-// One workgroup of 4 waves per (sequence, value head, 32-column slice of V):
+// One workgroup of 6 waves per (sequence, value head, 32-column slice of V):
 //   waves 0, 1  state waves: wave j owns columns 16j..16j+15 of the slice and all K
 //               rows of S (fp32 accumulators).  W, KgT, Qg and Aqk are stored as
 //               permuted row fragments (see pfrag_off), so S and V_new in accumulator
 //               layout are, converted to bf16 in place, the contraction operands of
 //               the next products: the whole chain W S -> V_new -> KgT V_new -> S runs
-//               inside one wave.
-//   wave 2      output wave: one step behind, O = Qg S + Aqk V_new for both column
-//               halves from the S and V_new the state waves hand over through LDS,
-//               with Qg and Aqk prefetched a step ahead into its own registers; O is
-//               staged in LDS and written as 16-byte row segments.
-//   wave 3      loader: streams each step's W, KgT, U slice and d into a 3-slot LDS
+//               inside one wave.  Each step reads all of its ring operands first, so
+//               the LDS latency is paid once per step rather than once per product.
+//   waves 2, 3  output waves, one step behind: wave o forms O = Qg S + Aqk V_new for
+//               chunk rows [o C/2, (o+1) C/2) and both column halves, from the S and
+//               V_new the state waves hand over through LDS, with its rows of Qg and
+//               Aqk prefetched a step ahead into its own registers; O is staged in LDS
+//               and written as 16-byte row segments.
+//   waves 4, 5  loaders: stream each step's W, KgT, U slice and d into a 3-slot LDS
 //               ring with direct global->LDS loads, two steps ahead of the state waves.
 // One barrier per step orders the ring, the hand-over buffers and the waves.
 //
@@ -35,22 +37,24 @@ namespace kda {
 template <int C, int K>
 struct RegRecur {
     static constexpr int NKK = K / 32, NMT = C / 16, NMS = C / 32, NT = K / 16;
-    static constexpr int NS = 3;  // ring slots
+    static constexpr int NS = 3;            // ring slots
+    static constexpr int NMO = NMT / 2;     // row tiles per output wave
     // one ring slot (bytes): W [NMT][NKK] and KgT [NT][NMS] fragment units of 1 KB, U for
     // the slice's two 16-column tiles ([2][NMT] quad units of 512 B), d [K] fp32
-    static constexpr size_t kW = 0, kKgT = kW + (size_t)C * K * 2, kU = kKgT + (size_t)K * C * 2;
-    static constexpr size_t kD = kU + (size_t)C * 32 * 2, kSlot = kD + (size_t)K * 4;
+    static constexpr int NLW = C * K * 2 / 1024, NLU = C * 32 * 2 / 1024;
+    static constexpr size_t kW = 0, kKgT = kW + (size_t)NLW * 1024, kU = kKgT + (size_t)NLW * 1024;
+    static constexpr size_t kD = kU + (size_t)NLU * 1024, kSlot = kD + (size_t)K * 4;
     // hand-over buffers [2][2 state waves]: S as [NKK] operand units, V_new as [NMS] units
     static constexpr size_t kExWave = (size_t)(NKK + NMS) * 1024;
     static constexpr size_t kEx = NS * kSlot, kOs = kEx + 4 * kExWave;
     static constexpr int LDO = kBV + 8;  // output tile row stride (bf16)
     static constexpr size_t kBytes = kOs + (size_t)C * LDO * 2;
-    // loader instructions per step: 1 KB units of W, KgT and U, then d as 16 bytes on
-    // each of the first K/4 lanes
-    static constexpr int NLW = C * K * 2 / 1024, NLU = C * 32 * 2 / 1024;
-    static constexpr int NLOAD = 2 * NLW + NLU + 1;
+    // 1 KB ring units per step, dealt to the two loader waves alternately; loader 1 also
+    // loads d (16 bytes on each of the first K/4 lanes)
+    static constexpr int NUNITS = 2 * NLW + NLU;
+    static constexpr int nload(int i) { return (NUNITS - i + 1) / 2 + (i == 1 ? 1 : 0); }
+    static_assert(nload(0) <= 31 && nload(1) <= 31, "loader wait count");
     static_assert(K / 4 <= 64, "d in one load");
-    static_assert(NLOAD <= 63, "loader wait count");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of this wave
@@ -65,11 +69,35 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
+// Loader wave I: its share of step k's ring loads (slot k % NS).
+template <int C, int K, int I>
+__device__ __forceinline__ void ring_issue(const Params &p, unsigned char *ring, size_t sl, int k, int v0, int l) {
+    using R = RegRecur<C, K>;
+    unsigned char *dst = ring + (size_t)(k % R::NS) * R::kSlot;
+    const unsigned char *gW = reinterpret_cast<const unsigned char *>(p.w_W) + sl * C * K * 2;
+    const unsigned char *gK = reinterpret_cast<const unsigned char *>(p.w_KgT) + sl * K * C * 2;
+    const unsigned char *gU =
+        reinterpret_cast<const unsigned char *>(p.w_U) + (sl * (size_t)p.V * C + quad_off(0, v0, C)) * 2;
+    const unsigned char *gD = reinterpret_cast<const unsigned char *>(p.w_d + sl * K);
+#pragma unroll
+    for (int u = I; u < R::NUNITS; u += 2) {
+        const unsigned char *src;
+        size_t off;
+        if (u < R::NLW) src = gW + u * 1024, off = R::kW + u * 1024;
+        else if (u < 2 * R::NLW) src = gK + (u - R::NLW) * 1024, off = R::kKgT + (u - R::NLW) * 1024;
+        else src = gU + (u - 2 * R::NLW) * 1024, off = R::kU + (u - 2 * R::NLW) * 1024;
+        lds_dma16(src + l * 16, dst + off);
+    }
+    if constexpr (I == 1) {
+        if (l < K / 4) lds_dma16(gD + l * 16, dst + R::kD);
+    }
+}
+
 template <int C, int NKK>
-__global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
+__global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))) recur_reg_kernel(Params p) {
     constexpr int K = 32 * NKK;
     using R = RegRecur<C, K>;
-    constexpr int NMT = R::NMT, NMS = R::NMS, NT = R::NT, NS = R::NS;
+    constexpr int NMT = R::NMT, NMS = R::NMS, NT = R::NT, NS = R::NS, NMO = R::NMO;
     extern __shared__ __align__(16) unsigned char lds[];
     const int V = p.V;
 
@@ -114,50 +142,69 @@ __global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
             const uint4 *Kr = reinterpret_cast<const uint4 *>(sl + R::kKgT);
             const uint2 *Ur = reinterpret_cast<const uint2 *>(sl + R::kU);
             const float4 *Dr = reinterpret_cast<const float4 *>(sl + R::kD);
+            // every ring operand of the step first
+            uint4 wf[NMT][NKK], kf[NT][NMS];
+            uint2 uq[NMT];
+            float4 dd[NT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) wf[mt][kk] = Wr[(mt * NKK + kk) * 64 + l];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) uq[mt] = Ur[(j * NMT + mt) * 64 + l];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) kf[t][ms] = Kr[(t * NMS + ms) * 64 + l];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) dd[t] = Dr[4 * t + cg];
+            __builtin_amdgcn_sched_barrier(0);
             uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
-            // S in bf16 as the contraction operand (permuted order), handed to the output wave
+            // S in bf16 as the contraction operand (permuted order), handed to the output waves
             uint4 Sb[NKK];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
+            for (int kk = 0; kk < NKK; ++kk)
                 Sb[kk] = make_uint4(pack2(S[2 * kk][0], S[2 * kk][1]), pack2(S[2 * kk][2], S[2 * kk][3]),
                                     pack2(S[2 * kk + 1][0], S[2 * kk + 1][1]),
                                     pack2(S[2 * kk + 1][2], S[2 * kk + 1][3]));
-                xs[kk * 64 + l] = Sb[kk];
-            }
             // V_new = U - W S  (accumulator layout: rows 16mt+4cg+jj, column lr)
+            f32x4 Pw[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) Pw[mt] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt) Pw[mt] = mma32_bf16(Pw[mt], wf[mt][kk], Sb[kk]);
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) xs[kk * 64 + l] = Sb[kk];
             f32x4 Vn[NMT];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) acc = mma32_bf16(acc, Wr[(mt * NKK + kk) * 64 + l], Sb[kk]);
-                const uint2 uq = Ur[(j * NMT + mt) * 64 + l];
-                Vn[mt][0] = __uint_as_float(uq.x << 16) - acc[0];
-                Vn[mt][1] = __uint_as_float(uq.x & 0xffff0000u) - acc[1];
-                Vn[mt][2] = __uint_as_float(uq.y << 16) - acc[2];
-                Vn[mt][3] = __uint_as_float(uq.y & 0xffff0000u) - acc[3];
+                Vn[mt][0] = __uint_as_float(uq[mt].x << 16) - Pw[mt][0];
+                Vn[mt][1] = __uint_as_float(uq[mt].x & 0xffff0000u) - Pw[mt][1];
+                Vn[mt][2] = __uint_as_float(uq[mt].y << 16) - Pw[mt][2];
+                Vn[mt][3] = __uint_as_float(uq[mt].y & 0xffff0000u) - Pw[mt][3];
             }
             uint4 Vb[NMS];
 #pragma unroll
-            for (int ms = 0; ms < NMS; ++ms) {
+            for (int ms = 0; ms < NMS; ++ms)
                 Vb[ms] = make_uint4(pack2(Vn[2 * ms][0], Vn[2 * ms][1]), pack2(Vn[2 * ms][2], Vn[2 * ms][3]),
                                     pack2(Vn[2 * ms + 1][0], Vn[2 * ms + 1][1]),
                                     pack2(Vn[2 * ms + 1][2], Vn[2 * ms + 1][3]));
-                xv[ms * 64 + l] = Vb[ms];
-            }
             // S <- Diag(d) S + KgT V_new
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const float4 dd = Dr[4 * t + cg];
-                f32x4 acc = S[t];
-                acc[0] *= dd.x;
-                acc[1] *= dd.y;
-                acc[2] *= dd.z;
-                acc[3] *= dd.w;
-#pragma unroll
-                for (int ms = 0; ms < NMS; ++ms) acc = mma32_bf16(acc, Kr[(t * NMS + ms) * 64 + l], Vb[ms]);
-                S[t] = acc;
+                S[t][0] *= dd[t].x;
+                S[t][1] *= dd[t].y;
+                S[t][2] *= dd[t].z;
+                S[t][3] *= dd[t].w;
             }
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) S[t] = mma32_bf16(S[t], kf[t][ms], Vb[ms]);
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) xv[ms * 64 + l] = Vb[ms];
         }
         if (p.output_final_state) {
 #pragma unroll
@@ -165,45 +212,51 @@ __global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) p.ht[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col] = S[t][jj];
         }
-    } else if (wid == 2) {
-        // ------------------------------------------------------------ output wave
-        // Qg / Aqk fragments for one step: Qg [NMT][NKK], Aqk [NMT][NMS] (only the
-        // blocks at or left of the diagonal are read)
+    } else if (wid < 4) {
+        // ------------------------------------------------------------ output wave o
+        const int o = wid - 2;
+        const int mt0 = o * NMO;
+        // this wave's rows of Qg [NMO][NKK] and of the non-zero Aqk blocks [NMO][NMS]
         struct QA {
-            uint4 q[NMT][NKK];
-            uint4 a[NMT][NMS];
+            uint4 q[NMO][NKK];
+            uint4 a[NMO][NMS];
         };
         auto load_qa = [&](QA &x, int k) {
             const size_t sl = slot_of(k);
             const uint4 *Qr = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w_Qg) + sl * C * K);
             const uint4 *Ar = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w_Aqk) + sl * C * C);
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
+            for (int mo = 0; mo < NMO; ++mo) {
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) x.q[mt][kk] = Qr[(mt * NKK + kk) * 64 + l];
+                for (int kk = 0; kk < NKK; ++kk) x.q[mo][kk] = Qr[((mt0 + mo) * NKK + kk) * 64 + l];
 #pragma unroll
                 for (int ms = 0; ms < NMS; ++ms)
-                    if (32 * ms <= 16 * mt + 15) x.a[mt][ms] = Ar[(mt * NMS + ms) * 64 + l];
+                    if (32 * ms <= 16 * (mt0 + mo) + 15) x.a[mo][ms] = Ar[((mt0 + mo) * NMS + ms) * 64 + l];
             }
         };
         auto out_step = [&](const QA &x, int k) {
-            // output of step k from hand-over buffer k & 1
+            // output rows of step k from hand-over buffer k & 1
+            uint4 Sb[2][NKK], Vb[2][NMS];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
-                uint4 Sb[NKK], Vb[NMS];
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) Sb[kk] = xs[kk * 64 + l];
+                for (int kk = 0; kk < NKK; ++kk) Sb[j][kk] = xs[kk * 64 + l];
 #pragma unroll
-                for (int ms = 0; ms < NMS; ++ms) Vb[ms] = xv[ms * 64 + l];
+                for (int ms = 0; ms < NMS; ++ms) Vb[j][ms] = xv[ms * 64 + l];
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < NMT; ++mt) {
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int mo = 0; mo < NMO; ++mo) {
+                    const int mt = mt0 + mo;
                     f32x4 acc = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) acc = mma32_bf16(acc, Sb[kk], x.q[mt][kk]);
+                    for (int kk = 0; kk < NKK; ++kk) acc = mma32_bf16(acc, Sb[j][kk], x.q[mo][kk]);
 #pragma unroll
                     for (int ms = 0; ms < NMS; ++ms)
-                        if (32 * ms <= 16 * mt + 15) acc = mma32_bf16(acc, Vb[ms], x.a[mt][ms]);
+                        if (32 * ms <= 16 * mt + 15) acc = mma32_bf16(acc, Vb[j][ms], x.a[mo][ms]);
                     // lane: row 16mt+lr, columns 16j+4cg..+3
                     *reinterpret_cast<uint2 *>(OS + (16 * mt + lr) * R::LDO + 16 * j + 4 * cg) =
                         make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
@@ -212,8 +265,8 @@ __global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
             const int64_t tok0 = sb + (int64_t)k * C;
             const int L = (int)((se - tok0) < C ? (se - tok0) : C);
 #pragma unroll
-            for (int it = 0; it < C / 16; ++it) {
-                const int m = 16 * it + (l >> 2), c8 = 8 * (l & 3);
+            for (int it = 0; it < NMO; ++it) {
+                const int m = 16 * mt0 + 16 * it + (l >> 2), c8 = 8 * (l & 3);
                 if (m < L)
                     *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.o) + ((tok0 + m) * p.HV + hv) * (int64_t)V +
                                                v0 + c8) = *reinterpret_cast<const uint4 *>(OS + m * R::LDO + c8);
@@ -235,27 +288,20 @@ __global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
             if (k >= 1) out_step(qa[1], k - 1);
         }
     } else {
-        // ------------------------------------------------------------ loader wave
+        // ------------------------------------------------------------ loader wave i
+        const int i = wid - 4;
         auto issue = [&](int k) {
-            const size_t sl = slot_of(k);
-            unsigned char *dst = ring + (size_t)(k % NS) * R::kSlot;
-            const unsigned char *gW = reinterpret_cast<const unsigned char *>(p.w_W) + sl * C * K * 2;
-            const unsigned char *gK = reinterpret_cast<const unsigned char *>(p.w_KgT) + sl * K * C * 2;
-            const unsigned char *gU = reinterpret_cast<const unsigned char *>(p.w_U) +
-                                      (sl * (size_t)V * C + quad_off(0, v0, C)) * 2;
-            const unsigned char *gD = reinterpret_cast<const unsigned char *>(p.w_d + sl * K);
-#pragma unroll
-            for (int i = 0; i < R::NLW; ++i) lds_dma16(gW + i * 1024 + l * 16, dst + R::kW + i * 1024);
-#pragma unroll
-            for (int i = 0; i < R::NLW; ++i) lds_dma16(gK + i * 1024 + l * 16, dst + R::kKgT + i * 1024);
-#pragma unroll
-            for (int i = 0; i < R::NLU; ++i) lds_dma16(gU + i * 1024 + l * 16, dst + R::kU + i * 1024);
-            if (l < K / 4) lds_dma16(gD + l * 16, dst + R::kD);
+            if (i == 0) ring_issue<C, K, 0>(p, ring, slot_of(k), k, v0, l);
+            else ring_issue<C, K, 1>(p, ring, slot_of(k), k, v0, l);
+        };
+        auto wait_one_step = [&]() {
+            if (i == 0) wait_vmcnt<R::nload(0)>();
+            else wait_vmcnt<R::nload(1)>();
         };
         if (nsteps > 0) issue(0);
         if (nsteps > 1) {
             issue(1);
-            wait_vmcnt<R::NLOAD>();
+            wait_one_step();
         } else {
             wait_vmcnt<0>();
         }
@@ -263,7 +309,7 @@ __global__ void __launch_bounds__(256) recur_reg_kernel(Params p) {
             __builtin_amdgcn_s_barrier();
             if (k + 2 < nsteps) {
                 issue(k + 2);
-                wait_vmcnt<R::NLOAD>();  // step k + 1 has landed
+                wait_one_step();  // step k + 1 has landed
             } else {
                 wait_vmcnt<0>();
             }
@@ -281,7 +327,7 @@ hipError_t launch_recur_reg(const Params &p, hipStream_t s) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
         if (e != hipSuccess) return;
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+        hipLaunchKernelGGL(kern, grid, dim3(384), lds, s, p);
         e = hipGetLastError();
     };
     switch (p.K / 32) {
