@@ -23,11 +23,25 @@ __device__ __forceinline__ int64_t seq_begin(const Params &p, int n) {
     return p.cu_seqlens ? p.cu_seqlens[n] : (int64_t)n * p.T;
 }
 
-// Global chunk gc -> its sequence, first token and length.  Chunks start at every
-// sequence start and then every C tokens, so a chunk never straddles sequences.
+// Chunks start at every sequence start and then every C tokens, so a chunk never
+// straddles sequences.  Without cu_seqlens every sequence has ceil(T / C) chunks and
+// the chunk tables are plain arithmetic; with it they come from the plan kernel.
+__device__ __forceinline__ int chunks_per_seq(const Params &p) { return (p.T + p.C - 1) / p.C; }
+__device__ __forceinline__ int seq_chunk_begin(const Params &p, int n) {
+    return p.cu_seqlens ? p.chunk_off[n] : n * chunks_per_seq(p);
+}
+
+// Global chunk gc -> its sequence, first token and length.
 __device__ __forceinline__ ChunkInfo chunk_info(const Params &p, int gc) {
-    const int n = p.chunk_seq[gc];
-    const int c = gc - p.chunk_off[n];
+    int n, c;
+    if (p.cu_seqlens) {
+        n = p.chunk_seq[gc];
+        c = gc - p.chunk_off[n];
+    } else {
+        const int nc = chunks_per_seq(p);
+        n = gc / nc;
+        c = gc - n * nc;
+    }
     const int64_t s0 = seq_begin(p, n);
     const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[n + 1] : s0 + p.T;
     const int64_t tok0 = s0 + (int64_t)c * p.C;

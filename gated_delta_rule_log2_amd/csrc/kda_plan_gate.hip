@@ -9,7 +9,8 @@
 namespace kda {
 
 // One workgroup of 256 threads: exclusive scan of per-sequence chunk counts into
-// chunk_off[0..N], then the inverse map chunk_seq[gc] = n.
+// chunk_off[0..N], then the inverse map chunk_seq[gc] = n by binary search.  Only
+// packed (cu_seqlens) batches need it; fixed-length batches compute both inline.
 __global__ void __launch_bounds__(256) plan_kernel(Params p) {
     __shared__ int warp_tot[4];
     __shared__ int carry_s;
@@ -41,9 +42,15 @@ __global__ void __launch_bounds__(256) plan_kernel(Params p) {
     }
     if (tid == 0) p.chunk_off[p.N] = carry_s;
     __syncthreads();
-    for (int n = tid; n < p.N; n += 256) {
-        const int a = p.chunk_off[n], b = p.chunk_off[n + 1];
-        for (int c = a; c < b; ++c) p.chunk_seq[c] = n;
+    const int total = carry_s;
+    for (int gc = tid; gc < total; gc += 256) {
+        int lo = 0, hi = p.N - 1;  // last n with chunk_off[n] <= gc (empty sequences skipped)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.chunk_off[mid] <= gc) lo = mid;
+            else hi = mid - 1;
+        }
+        p.chunk_seq[gc] = lo;
     }
 }
 
@@ -74,6 +81,7 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(Params p) {
 }
 
 hipError_t launch_plan(const Params &p, hipStream_t s) {
+    if (!p.cu_seqlens) return hipSuccess;  // fixed-length batches need no tables
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
     return hipGetLastError();
 }

@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(512) recur_kernel(Params p) {
     const bool row_wave = w < C / 16;
     const StepCtx<C, T, NKK> x{ST, VT, OS, w, lr, cg, hv, v0, row_wave};
 
-    const int c0 = p.chunk_off[n], c1 = p.chunk_off[n + 1];
+    const int c0 = seq_chunk_begin(p, n), c1 = seq_chunk_begin(p, n + 1);
     const int64_t sb = seq_begin(p, n);
     const int64_t se = p.cu_seqlens ? p.cu_seqlens[n + 1] : sb + p.T;
     auto tok_of = [&](int g) { return sb + (int64_t)(g - c0) * C; };

@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int v0 = kBV * (pos % nvt);
     const int wid = threadIdx.x >> 6, l = lane_id(), lr = l & 15, cg = l >> 4;
 
-    const int c0 = p.chunk_off[n], c1 = p.chunk_off[n + 1];
+    const int c0 = seq_chunk_begin(p, n), c1 = seq_chunk_begin(p, n + 1);
     const int nsteps = c1 - c0;
     const int64_t sb = seq_begin(p, n);
     const int64_t se = p.cu_seqlens ? p.cu_seqlens[n + 1] : sb + p.T;
