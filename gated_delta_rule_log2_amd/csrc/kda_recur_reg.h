@@ -7,7 +7,7 @@
 //   V_new = U - W S,   O = Qg S + Aqk V_new (S before the update),
 //   S <- Diag(d) S + KgT V_new,   d = 2^G_last
 //
-// One workgroup of 6 waves per (sequence, value head, 32-column slice of V):
+// One workgroup of 4 + C/16 waves per (sequence, value head, 32-column slice of V):
 //   waves 0, 1  state waves: wave j owns columns 16j..16j+15 of the slice and all K
 //               rows of S (fp32 accumulators).  W, KgT, Qg and Aqk are stored as
 //               permuted row fragments (see pfrag_off), so S and V_new in accumulator
@@ -15,13 +15,16 @@
 //               the next products: the whole chain W S -> V_new -> KgT V_new -> S runs
 //               inside one wave.  Each step reads all of its ring operands first, so
 //               the LDS latency is paid once per step rather than once per product.
-//   waves 2, 3  output waves, one step behind: wave o forms O = Qg S + Aqk V_new for
-//               chunk rows [o C/2, (o+1) C/2) and both column halves, from the S and
-//               V_new the state waves hand over through LDS, with its rows of Qg and
-//               Aqk prefetched a step ahead into its own registers; O is staged in LDS
+//   C/16 output waves, one step behind: output wave o forms O = Qg S + Aqk V_new for
+//               chunk rows 16o..16o+15 and both column halves, from the S and V_new
+//               the state waves hand over through LDS, with its rows of Qg and Aqk
+//               prefetched a step ahead into its own registers; O is staged in LDS
 //               and written as 16-byte row segments.
-//   waves 4, 5  loaders: stream each step's W, KgT, U slice and d into a 3-slot LDS
-//               ring with direct global->LDS loads, two steps ahead of the state waves.
+//   2 loaders   stream each step's W, KgT, U slice and d into a 3-slot LDS ring with
+//               direct global->LDS loads, two steps ahead of the state waves.
+// Waves are dealt to the 4 SIMDs round-robin by index; the roles are numbered so the
+// two state waves share their SIMDs only with the loaders (their matrix-core chain is
+// the critical path) and the output waves take the other two SIMDs.
 // One barrier per step orders the ring, the hand-over buffers and the waves.
 //
 // Placement: workgroups are dealt to the 8 XCDs round-robin by index; the index is
@@ -38,7 +41,8 @@ template <int C, int K>
 struct RegRecur {
     static constexpr int NKK = K / 32, NMT = C / 16, NMS = C / 32, NT = K / 16;
     static constexpr int NS = 3;            // ring slots
-    static constexpr int NMO = NMT / 2;     // row tiles per output wave
+    static constexpr int NMO = 1;           // row tiles per output wave
+    static constexpr int NWAVES = 4 + NMT;  // 2 state, NMT output, 2 loader waves
     // one ring slot (bytes): W [NMT][NKK] and KgT [NT][NMS] fragment units of 1 KB, U for
     // the slice's two 16-column tiles ([2][NMT] quad units of 512 B), d [K] fp32
     static constexpr int NLW = C * K * 2 / 1024, NLU = C * 32 * 2 / 1024;
@@ -94,7 +98,8 @@ __device__ __forceinline__ void ring_issue(const Params &p, unsigned char *ring,
 }
 
 template <int C, int NKK>
-__global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))) recur_reg_kernel(Params p) {
+__global__ void __launch_bounds__(64 * (4 + C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+recur_reg_kernel(Params p) {
     constexpr int K = 32 * NKK;
     using R = RegRecur<C, K>;
     constexpr int NMT = R::NMT, NMS = R::NMS, NT = R::NT, NS = R::NS, NMO = R::NMO;
@@ -109,6 +114,9 @@ __global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n = u / p.HV, hv = u % p.HV;
     const int v0 = kBV * (pos % nvt);
     const int wid = threadIdx.x >> 6, l = lane_id(), lr = l & 15, cg = l >> 4;
+    // roles: waves 0, 1 state; 4, 5 loaders; 2, 3 and (C = 64) 6, 7 output
+    const bool is_state = wid < 2, is_loader = wid == 4 || wid == 5;
+    const int out_idx = wid < 4 ? wid - 2 : wid - 4;
 
     const int c0 = seq_chunk_begin(p, n), c1 = seq_chunk_begin(p, n + 1);
     const int nsteps = c1 - c0;
@@ -120,7 +128,7 @@ __global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto ex_v = [&](int e, int j) { return ex_s(e, j) + NKK * 64; };
     uint16_t *OS = reinterpret_cast<uint16_t *>(lds + R::kOs);
 
-    if (wid < 2) {
+    if (is_state) {
         // ------------------------------------------------------------ state wave j
         const int j = wid;
         const int col = v0 + 16 * j + lr;
@@ -212,9 +220,9 @@ __global__ void __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) p.ht[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col] = S[t][jj];
         }
-    } else if (wid < 4) {
+    } else if (!is_loader) {
         // ------------------------------------------------------------ output wave o
-        const int o = wid - 2;
+        const int o = out_idx;
         const int mt0 = o * NMO;
         // this wave's rows of Qg [NMO][NKK] and of the non-zero Aqk blocks [NMO][NMS]
         struct QA {
@@ -327,7 +335,7 @@ hipError_t launch_recur_reg(const Params &p, hipStream_t s) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
         if (e != hipSuccess) return;
-        hipLaunchKernelGGL(kern, grid, dim3(384), lds, s, p);
+        hipLaunchKernelGGL(kern, grid, dim3(64 * (4 + C / 16)), lds, s, p);
         e = hipGetLastError();
     };
     switch (p.K / 32) {
