@@ -488,43 +488,51 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             }
         }
     }
-    const int nms = (16 * w + 16 + 31) / 32;
-    uint4 am[2];
+    // rows of A Diag(b) as bf16 operands: row block w for W, row block NB-1-w for U, so
+    // every wave does the same number of products (block b needs (b+2)/2 32-column spans)
+    const int bw = w, bu = NB - 1 - w;
+    const int nmw = (16 * bw + 16 + 31) / 32, nmu = (16 * bu + 16 + 31) / 32;
+    auto a_rows = [&](int b, int nm, uint4 (&am)[2]) {
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-        if (ms < nms) {
-            float a8[8], b8[8];
-            load8(Ainv + (16 * w + lr) * LDA + 32 * ms + 8 * cg, a8);
-            load8(betas + 32 * ms + 8 * cg, b8);
+        for (int ms = 0; ms < 2; ++ms) {
+            if (ms < nm) {
+                float a8[8], b8[8];
+                load8(Ainv + (16 * b + lr) * LDA + 32 * ms + 8 * cg, a8);
+                load8(betas + 32 * ms + 8 * cg, b8);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a8[i] *= b8[i];
-            am[ms] = pack8(a8);
-        } else {
-            am[ms] = make_uint4(0u, 0u, 0u, 0u);
+                for (int i = 0; i < 8; ++i) a8[i] *= b8[i];
+                am[ms] = pack8(a8);
+            } else {
+                am[ms] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
-    }
+    };
+    uint4 amw[2], amu[2];
+    a_rows(bw, nmw, amw);
+    a_rows(bu, nmu, amu);
     __syncthreads();
 
-    // ---- step 8: W = A Diag(b) X (lane: row m = 16w+lr, columns 16dt+4cg..),
-    //      U = A Diag(b) v (lane: rows m = 16w+4cg.., column 16vt+lr) ----
+    // ---- step 8: W = A Diag(b) X (lane: row m = 16bw+lr, columns 16dt+4cg..),
+    //      U = A Diag(b) v (lane: rows m = 16bu+4cg.., column 16vt+lr) ----
     for (int dt = 0; dt < K / 16; ++dt) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
-            if (ms < nms)
+            if (ms < nmw)
                 acc = mma32_bf16(acc, *reinterpret_cast<const uint4 *>(XT + swz<C>(16 * dt + lr, 32 * ms + 8 * cg)),
-                                 am[ms]);
-        *reinterpret_cast<uint2 *>(Wg + (PERM ? pfrag_off(r, 16 * dt + 4 * cg, K) : frag_off(r, 16 * dt + 4 * cg, K))) =
+                                 amw[ms]);
+        const int rw = 16 * bw + lr;
+        *reinterpret_cast<uint2 *>(Wg + (PERM ? pfrag_off(rw, 16 * dt + 4 * cg, K) : frag_off(rw, 16 * dt + 4 * cg, K))) =
             make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
     for (int vt = 0; vt < V / 16; ++vt) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
-            if (ms < nms)
-                acc = mma32_bf16(acc, am[ms],
+            if (ms < nmu)
+                acc = mma32_bf16(acc, amu[ms],
                                  *reinterpret_cast<const uint4 *>(VT + swz<C>(16 * vt + lr, 32 * ms + 8 * cg)));
-        *reinterpret_cast<uint2 *>(UTg + quad_off(16 * w + 4 * cg, 16 * vt + lr, C)) =
+        *reinterpret_cast<uint2 *>(UTg + quad_off(16 * bu + 4 * cg, 16 * vt + lr, C)) =
             make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
 }
