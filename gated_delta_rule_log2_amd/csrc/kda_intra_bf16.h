@@ -405,6 +405,7 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(KST + swz<C>(d, m0));
         }
     }
+    uint2 aqp[NB];
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
         float aq[4], ak[4];
@@ -415,9 +416,19 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             aq[jj] = (s < w || (s == w && jl <= lr)) ? vq[jj] : 0.f;
             ak[jj] = (s < w || (s == w && jl < lr)) ? b_r * vk[jj] : 0.f;
         }
-        *reinterpret_cast<uint2 *>(Aqkg + (PERM ? pfrag_off(r, 16 * s + 4 * cg, C) : frag_off(r, 16 * s + 4 * cg, C))) =
-            make_uint2(pack2(aq[0], aq[1]), pack2(aq[2], aq[3]));
+        aqp[s] = make_uint2(pack2(aq[0], aq[1]), pack2(aq[2], aq[3]));
         store4(Akk + r * LDA + 16 * s + 4 * cg, ak[0], ak[1], ak[2], ak[3]);
+    }
+    if constexpr (PERM) {
+        // columns 16s + 4cg.. of blocks 2m and 2m + 1 are adjacent 8-byte halves of one
+        // 16-byte unit: one full store per block pair
+#pragma unroll
+        for (int m = 0; m < NB / 2; ++m)
+            *reinterpret_cast<uint4 *>(Aqkg + pfrag_off(r, 32 * m + 4 * cg, C)) =
+                make_uint4(aqp[2 * m].x, aqp[2 * m].y, aqp[2 * m + 1].x, aqp[2 * m + 1].y);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) *reinterpret_cast<uint2 *>(Aqkg + frag_off(r, 16 * s + 4 * cg, C)) = aqp[s];
     }
     // v rows for U: the first four 32-column slices are loaded now, so their latency
     // overlaps the solve
@@ -514,16 +525,26 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 
     // ---- step 8: W = A Diag(b) X (lane: row m = 16bw+lr, columns 16dt+4cg..),
     //      U = A Diag(b) v (lane: rows m = 16bu+4cg.., column 16vt+lr) ----
-    for (int dt = 0; dt < K / 16; ++dt) {
-        f32x4 acc = zero4();
+    const int rw = 16 * bw + lr;
+    for (int dp = 0; dp < K / 32; ++dp) {
+        uint2 wq[2];
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-            if (ms < nmw)
-                acc = mma32_bf16(acc, *reinterpret_cast<const uint4 *>(XT + swz<C>(16 * dt + lr, 32 * ms + 8 * cg)),
-                                 amw[ms]);
-        const int rw = 16 * bw + lr;
-        *reinterpret_cast<uint2 *>(Wg + (PERM ? pfrag_off(rw, 16 * dt + 4 * cg, K) : frag_off(rw, 16 * dt + 4 * cg, K))) =
-            make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+        for (int hh = 0; hh < 2; ++hh) {
+            const int dt = 2 * dp + hh;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+                if (ms < nmw)
+                    acc = mma32_bf16(acc, *reinterpret_cast<const uint4 *>(XT + swz<C>(16 * dt + lr, 32 * ms + 8 * cg)),
+                                     amw[ms]);
+            wq[hh] = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+        }
+        if constexpr (PERM) {  // the two 16-column tiles fill one 16-byte unit
+            *reinterpret_cast<uint4 *>(Wg + pfrag_off(rw, 32 * dp + 4 * cg, K)) = make_uint4(wq[0].x, wq[0].y, wq[1].x, wq[1].y);
+        } else {
+            *reinterpret_cast<uint2 *>(Wg + frag_off(rw, 32 * dp + 4 * cg, K)) = wq[0];
+            *reinterpret_cast<uint2 *>(Wg + frag_off(rw, 32 * dp + 16 + 4 * cg, K)) = wq[1];
+        }
     }
     for (int vt = 0; vt < V / 16; ++vt) {
         f32x4 acc = zero4();
