@@ -106,12 +106,17 @@ struct IntraBf16Lds {
 #define KDA_INTRA_OCC
 #endif
 
+// Zero gate bias read in place of a missing dt_bias, so the bias loads need no branch
+// (a branch around them makes the compiler wait for them before the q/k loads issue).
+static __device__ float kda_zero_bias[256];
+
 // Key widths up to 128 store W, Qg, Aqk and KgT as permuted row fragments (the
 // layout of the register-resident recurrence); wider keys keep plain row fragments.
 template <int K>
 __host__ __device__ constexpr bool permuted_layout() { return K <= 128; }
 
-template <int C, int NKK>
+// GB, BB: gate input, beta stored as bf16 (else fp32)
+template <int C, int NKK, bool GB, bool BB>
 __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(Params p) {
     constexpr int NB = C / 16, K = 32 * NKK;
     constexpr bool PERM = permuted_layout<K>();
@@ -156,24 +161,54 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     uint16_t *Aqkg = static_cast<uint16_t *>(p.w_Aqk) + slot * C * C;
     float *dg = p.w_d + slot * K;
 
-    // ---- loads: q, k (packed bf16), gate, beta ----
+    // ---- loads: gate and beta first (the gate math and scan start as soon as they land,
+    //      while q and k are still in flight), then q, k (packed bf16) ----
     const int64_t qkrow = ((ci.tok0 + rl) * p.H + h) * (int64_t)K + 8 * cg;
     const int64_t grow = ((ci.tok0 + rl) * p.HV + hv) * (int64_t)K + 8 * cg;
+    // raw gate words (bf16: one 16-byte unit per 8 values; fp32: two) and raw beta bits,
+    // widened only after the q/k loads are issued, so no wait sits between the loads
+    uint4 graw[NKK][GB ? 1 : 2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (GB) {
+            graw[kk][0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.g) + grow + 32 * kk);
+        } else {
+            graw[kk][0] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.g) + grow + 32 * kk);
+            graw[kk][1] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.g) + grow + 32 * kk + 4);
+        }
+    }
+    // dt_bias for this lane's 8-column groups (read by both activated-gate forms)
+    static_assert(K <= 256, "zero bias size");
+    const float *dtb_row = p.dt_bias ? p.dt_bias + (int64_t)hv * K : kda_zero_bias;
+    float4 dtbv[NKK][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        dtbv[kk][0] = *reinterpret_cast<const float4 *>(dtb_row + 32 * kk + 8 * cg);
+        dtbv[kk][1] = *reinterpret_cast<const float4 *>(dtb_row + 32 * kk + 8 * cg + 4);
+    }
+    const int64_t bidx = (ci.tok0 + rl) * p.HV + hv;
+    uint32_t bbits;
+    if constexpr (BB) bbits = static_cast<const uint16_t *>(p.beta)[bidx];
+    else bbits = __float_as_uint(static_cast<const float *>(p.beta)[bidx]);
     uint4 qv[NKK], kv[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         qv[kk] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) + qkrow + 32 * kk);
         kv[kk] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.k) + qkrow + 32 * kk);
     }
+    const float braw = __uint_as_float(BB ? bbits << 16 : bbits);
     float G[NKK][8];
-    if (p.g_bf16) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) load8(static_cast<const uint16_t *>(p.g) + grow + 32 * kk, G[kk]);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) load8(static_cast<const float *>(p.g) + grow + 32 * kk, G[kk]);
+    for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (GB) {
+            unpack8(graw[kk][0], G[kk]);
+        } else {
+            const uint4 a = graw[kk][0], b = graw[kk][1];
+            G[kk][0] = __uint_as_float(a.x), G[kk][1] = __uint_as_float(a.y), G[kk][2] = __uint_as_float(a.z);
+            G[kk][3] = __uint_as_float(a.w), G[kk][4] = __uint_as_float(b.x), G[kk][5] = __uint_as_float(b.y);
+            G[kk][6] = __uint_as_float(b.z), G[kk][7] = __uint_as_float(b.w);
+        }
     }
-    const float braw = load_any(p.beta, (ci.tok0 + rl) * p.HV + hv, p.beta_bf16);
 
     // ---- step 1: activated gate in log2 units, 16-row inclusive scan ----
     if (p.gate_mode == kGateLowerBound) {
@@ -182,12 +217,8 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
         const float lb = valid ? p.lower_bound_log2 : 0.f;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            float dtb[8];
-            if (p.dt_bias) load8(p.dt_bias + (int64_t)hv * K + 32 * kk + 8 * cg, dtb);
-            else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dtb[i] = 0.f;
-            }
+            const float dtb[8] = {dtbv[kk][0].x, dtbv[kk][0].y, dtbv[kk][0].z, dtbv[kk][0].w,
+                                  dtbv[kk][1].x, dtbv[kk][1].y, dtbv[kk][1].z, dtbv[kk][1].w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float z = (G[kk][i] + dtb[i]) * aL;
@@ -199,12 +230,8 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
         const float s = valid ? kLog2e : 0.f;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            float dtb[8];
-            if (p.dt_bias) load8(p.dt_bias + (int64_t)hv * K + 32 * kk + 8 * cg, dtb);
-            else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dtb[i] = 0.f;
-            }
+            const float dtb[8] = {dtbv[kk][0].x, dtbv[kk][0].y, dtbv[kk][0].z, dtbv[kk][0].w,
+                                  dtbv[kk][1].x, dtbv[kk][1].y, dtbv[kk][1].z, dtbv[kk][1].w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[kk][i] = s * gate_natural(kGateSoftplus, G[kk][i], dtb[i], a, 0.f);
         }
@@ -561,7 +588,8 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 template <int C, int NKK>
 hipError_t launch_intra_bf16_t(const Params &p, hipStream_t s) {
     const size_t lds = IntraBf16Lds<C, 32 * NKK>::bytes(p.V);
-    auto kern = intra_bf16_kernel<C, NKK>;
+    auto kern = p.g_bf16 ? (p.beta_bf16 ? intra_bf16_kernel<C, NKK, true, true> : intra_bf16_kernel<C, NKK, true, false>)
+                         : (p.beta_bf16 ? intra_bf16_kernel<C, NKK, false, true> : intra_bf16_kernel<C, NKK, false, false>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
