@@ -552,7 +552,10 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 
     // ---- step 8: W = A Diag(b) X (lane: row m = 16bw+lr, columns 16dt+4cg..),
     //      U = A Diag(b) v (lane: rows m = 16bu+4cg.., column 16vt+lr) ----
+    // (loops unrolled so each wave's LDS operand reads are in flight together rather than
+    // one read-multiply-store round trip per tile)
     const int rw = 16 * bw + lr;
+#pragma unroll
     for (int dp = 0; dp < K / 32; ++dp) {
         uint2 wq[2];
 #pragma unroll
@@ -573,15 +576,23 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             *reinterpret_cast<uint2 *>(Wg + frag_off(rw, 32 * dp + 16 + 4 * cg, K)) = wq[1];
         }
     }
-    for (int vt = 0; vt < V / 16; ++vt) {
-        f32x4 acc = zero4();
+    for (int vt0 = 0; vt0 < V / 16; vt0 += 2) {  // V is a multiple of 32
+        uint4 vb[2][2];
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-            if (ms < nmu)
-                acc = mma32_bf16(acc, amu[ms],
-                                 *reinterpret_cast<const uint4 *>(VT + swz<C>(16 * vt + lr, 32 * ms + 8 * cg)));
-        *reinterpret_cast<uint2 *>(UTg + quad_off(16 * bu + 4 * cg, 16 * vt + lr, C)) =
-            make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+                vb[hh][ms] = ms < nmu ? *reinterpret_cast<const uint4 *>(VT + swz<C>(16 * (vt0 + hh) + lr, 32 * ms + 8 * cg))
+                                      : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+                if (ms < nmu) acc = mma32_bf16(acc, amu[ms], vb[hh][ms]);
+            *reinterpret_cast<uint2 *>(UTg + quad_off(16 * bu + 4 * cg, 16 * (vt0 + hh) + lr, C)) =
+                make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+        }
     }
 }
 
