@@ -142,11 +142,27 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     uint16_t *VT = reinterpret_cast<uint16_t *>(lds + L_::kVt);
     auto pair_of = [](int wb, int sb) { return wb * (wb - 1) / 2 + sb; };
 
-    const int hv = blockIdx.x % p.HV;
-    // chunks are taken last-to-first, so the first chunks the recurrence reads are the
-    // most recently written ones (still in the memory-side cache)
-    const int gc = p.total_chunks - 1 - (int)(blockIdx.x / p.HV);
-    const int h = hv / p.group;
+    // Workgroup b runs on XCD b % 8.  The value heads of one qk head (which read the same
+    // q and k rows) are given indices 8 apart, so they run on one XCD at about the same
+    // time and the second one finds q and k in that XCD's L2.  Chunks are taken
+    // last-to-first, so the first chunks the recurrence reads are the most recently
+    // written ones (still in the memory-side cache).
+    int qi, j;  // (chunk, qk head) item and the value head within its group
+    {
+        const int b = blockIdx.x, tile = 8 * p.group;
+        const int nq = p.total_chunks * p.H, full = nq / 8;
+        if (b < full * tile) {
+            qi = 8 * (b / tile) + (b % 8);
+            j = (b % tile) / 8;
+        } else {
+            const int rb = b - full * tile;
+            qi = 8 * full + rb / p.group;
+            j = rb % p.group;
+        }
+    }
+    const int gc = p.total_chunks - 1 - qi / p.H;
+    const int h = qi % p.H;
+    const int hv = h * p.group + j;
     const ChunkInfo ci = chunk_info(p, gc);
     const int w = threadIdx.x >> 6;
     const int l = lane_id(), lr = l & 15, cg = l >> 4;
