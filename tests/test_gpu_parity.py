@@ -59,6 +59,10 @@ SMALL = [
     TRAINING_BF16.replace(name="training_small", T=300, H=2, HV=2),
     GVA_BF16.replace(name="gva_small", T=517, H=2, HV=4),
     GVA_BF16.replace(name="gva_small_c32", T=333, H=2, HV=4, chunk=32),
+    # GVA groups of 3 and 4 value heads: the intra kernel places a group's workgroups
+    # 8 indices apart (tiled part and tail of the index map)
+    GVA_BF16.replace(name="gva3_small", T=333, H=3, HV=9),
+    GVA_BF16.replace(name="gva4_small", T=300, H=2, HV=8),
     VARLEN_BF16.replace(name="varlen_small", num_seqs=6, min_len=1, max_len=300, H=2, HV=4),
     LONG_BF16.replace(name="long_small", T=600, H=2, HV=2),
     TRAINING_BF16.replace(name="k256_v256", T=150, H=1, HV=2, K=256, V=256),
