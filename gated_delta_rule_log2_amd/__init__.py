@@ -25,7 +25,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_kda", "gate_chunk_cumsum", "KDAContractError", "KDARuntimeError",
+__all__ = ["chunk_kda", "fused_recurrent_kda", "gate_chunk_cumsum", "KDAContractError", "KDARuntimeError",
            "workspace_bytes", "library"]
 
 
@@ -214,6 +214,54 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     rc = lib.kda_chunk_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
                            _ptr(ht), _ptr(workspace), workspace.numel(), stream)
+    if rc != _abi.KDA_OK:
+        _raise(rc, lib)
+    return o, ht
+
+
+def fused_recurrent_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, scale: Optional[float] = None,
+                        initial_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
+                        cu_seqlens: Optional[torch.Tensor] = None, use_qk_l2norm_in_kernel: bool = False,
+                        use_gate_in_kernel: bool = False, safe_gate: bool = False,
+                        lower_bound: Optional[float] = None, A_log: Optional[torch.Tensor] = None,
+                        dt_bias: Optional[torch.Tensor] = None, use_beta_sigmoid_in_kernel: bool = False,
+                        allow_neg_eigval: bool = False):
+    """Token-by-token KDA forward (decoding) on the current HIP stream.
+
+    Same arguments, shapes and result as chunk_kda; the state stays on chip for each
+    sequence and there is no workspace.  Returns (o, final_state or None).
+    """
+    lib = library()
+    if q.dim() != 4 or v.dim() != 4:
+        raise KDAContractError(_abi.STATUS["KDA_ERR_SHAPE"], "q, k, v must be 4-D [B, T, heads, dim]")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KDARuntimeError(_abi.KDA_ERR_HIP, "fused_recurrent_kda runs on a HIP device; got a CPU tensor")
+    scale = 1.0 / math.sqrt(K) if scale is None else float(scale)
+    _check_tensor(k, "k", (B, T, H, K), dev, q.dtype)
+    _check_tensor(v, "v", (B, T, HV, V), dev, q.dtype)
+    _check_tensor(q, "q", (B, T, H, K), dev)
+    _check_tensor(g, "g", (B, T, HV, K), dev)
+    _check_tensor(beta, "beta", (B, T, HV), dev)
+    _check_tensor(A_log, "A_log", (HV,), dev, torch.float32)
+    _check_tensor(dt_bias, "dt_bias", (HV * K,), dev, torch.float32)
+    flags = _flags(use_gate_in_kernel, safe_gate, lower_bound, use_qk_l2norm_in_kernel,
+                   use_beta_sigmoid_in_kernel, allow_neg_eigval, output_final_state)
+    desc = _Desc(q, v, g, beta, scale, 64, cu_seqlens, lower_bound, flags)
+    N = desc.N
+    _check_tensor(initial_state, "initial_state", (N, HV, K, V), dev, torch.float32)
+    cu_dev = None
+    if cu_seqlens is not None:
+        cu_dev = cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    o = torch.empty((B, T, HV, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    rc = lib.kda_fused_recurrent_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
+                                     _ptr(ht), stream)
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
     return o, ht

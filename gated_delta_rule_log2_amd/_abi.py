@@ -31,7 +31,7 @@ OUTPUT_FINAL_STATE = 1 << 6
 EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
     "kda_gate_chunk_cumsum_workspace_size", "kda_gate_chunk_cumsum", "kda_chunk_fwd_stage_count",
-    "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled",
+    "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd",
 )
 
 
@@ -81,6 +81,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_profiled.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp, _vp]
     lib.kda_chunk_fwd_stage_count.restype = ctypes.c_int
+    lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_fused_recurrent_fwd.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.kda_chunk_fwd_stage_count.argtypes = []
     lib.kda_chunk_fwd_stage_name.restype = ctypes.c_char_p
     lib.kda_chunk_fwd_stage_name.argtypes = [ctypes.c_int]

@@ -211,6 +211,26 @@ kda_status kda_chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, co
                                   final_state, workspace, workspace_bytes, stream, nullptr);
 }
 
+kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
+                                   const void *g, const void *beta, const float *A_log, const float *dt_bias,
+                                   const float *initial_state, const int64_t *cu_seqlens, void *o,
+                                   float *final_state, hipStream_t stream) {
+    Params p;
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    const bool tokens = (int64_t)d->B * d->T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_OUTPUT_FINAL_STATE) && !final_state) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
+        return KDA_ERR_MISSING_A_LOG;
+    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.A_log = A_log; p.dt_bias = dt_bias; p.h0 = initial_state;
+    p.cu_seqlens = cu_seqlens;
+    p.o = o; p.ht = final_state;
+    return to_status(launch_fused_recurrent(p, stream));
+}
+
 kda_status kda_gate_chunk_cumsum(const kda_fwd_desc *d, const void *g, const float *A_log,
                                  const float *dt_bias, const int64_t *cu_seqlens, float *g_act,
                                  float *g_cum_log2, void *workspace, size_t workspace_bytes,

@@ -53,5 +53,6 @@ hipError_t launch_plan(const Params &p, hipStream_t s);
 hipError_t launch_gate_cumsum(const Params &p, hipStream_t s);
 hipError_t launch_intra(const Params &p, hipStream_t s);
 hipError_t launch_recurrence(const Params &p, hipStream_t s);
+hipError_t launch_fused_recurrent(const Params &p, hipStream_t s);
 
 }  // namespace kda

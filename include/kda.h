@@ -151,6 +151,28 @@ kda_status kda_chunk_fwd(const kda_fwd_desc *d,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fused_recurrent_kda forward: the token-by-token form of the same operator, the
+ * public entry for autoregressive decoding ("flash-linear-attention KDA 内核工程实践…",
+ * §1).  Per token, with the state stored [K][V]:
+ *   S <- Diag(exp(g')) S;  u = S^T k^;  S <- S + beta k^ (v - u)^T;  o = S^T q^
+ * ("Reading Notes: Implementation Notes for KDA in FLA", forward), g' the activated
+ * gate of kda_chunk_fwd, q^ = scale * q (L2-normalised first with
+ * KDA_QK_L2NORM), k^ = k (likewise normalised).
+ *
+ * Arguments, layouts, flags and error codes are those of kda_chunk_fwd; there is no
+ * workspace.  The descriptor passes the same checks (so chunk_size must still be 32
+ * or 64 although the token recurrence does not use it, and KDA_SAFE_GATE still
+ * validates the lower bound).  Each (sequence, value head) keeps its state on chip
+ * for the whole sequence, so the cost grows with T token by token: meant for
+ * decoding steps and short prompts, not for long prefill (use kda_chunk_fwd there).
+ */
+kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *A_log, const float *dt_bias,
+                                   const float *initial_state, const int64_t *cu_seqlens,
+                                   void *o, float *final_state, hipStream_t stream);
+
+/*
  * Stage introspection for profiling.  kda_chunk_fwd enqueues
  * kda_chunk_fwd_stage_count() kernels in order; kda_chunk_fwd_stage_name(i)
  * names stage i (NULL when i is out of range).
