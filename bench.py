@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "chunk_kda fwd Mtokens/s at HV=32,K=V=128,T=8K; % of MFMA/HBM roofline"
+METRIC_RECURRENT = "fused_recurrent_kda decode Mtokens/s; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 
@@ -115,6 +116,49 @@ def load_traffic(kernel: str, per_launch_bytes_alg: float):
     return int(entry["fetch_kib"] * 1024 * t["copy_factor_fetch"] + entry["write_kib"] * 1024 * t["copy_factor_write"])
 
 
+def bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip):
+    """Times kda_fused_recurrent_fwd (one kernel) and prints its own JSON line."""
+    import torch
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    rargs = (ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["g"]), ptr(d["beta"]), ptr(d["A_log"]),
+             ptr(d["dt_bias"]), ptr(d["initial_state"]), ptr(d["cu_seqlens"]), ptr(o), ptr(ht), stream)
+    for _ in range(args.warmup):
+        assert lib.kda_fused_recurrent_fwd(ctypes.byref(desc), *rargs) == 0
+    torch.cuda.synchronize()
+    start, end = hip.event(), hip.event()
+    t_wall = time.perf_counter()
+    hip.record(start, stream)
+    for _ in range(args.steps):
+        assert lib.kda_fused_recurrent_fwd(ctypes.byref(desc), *rargs) == 0
+    hip.record(end, stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = hip.elapsed_ms(start, end) / args.steps
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    ntok = B * T
+    alg_bytes = algorithmic_bytes(w, inp)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_RECURRENT, "value": round(ntok / (ms * 1e-3) / 1e6, 3), "unit": "Mtokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V,
+                   "sequences": len(inp["seq_lens"]), "initial_state": d["initial_state"] is not None,
+                   "final_state": w.output_final_state},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "fused_recurrent",
+                     "kernel_ms": round(ms, 5)},
+        "path": {"algorithmic_bytes": alg_bytes, "host_wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(w, inp, kw):
     from oracle import oracle_num_threads
     from tests.oracle_adapter import run_oracle
@@ -135,6 +179,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gva_bf16")
+    ap.add_argument("--entry", choices=("chunk", "recurrent"), default="chunk",
+                    help="chunk: kda_chunk_fwd (the metric); recurrent: kda_fused_recurrent_fwd, "
+                         "the token-by-token decoding entry (use with --workload decode_bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (5 times), the known-size "
@@ -208,6 +255,8 @@ def main() -> int:
              ptr(ws), ws.numel(), stream)
     nst = lib.kda_chunk_fwd_stage_count()
     names = [lib.kda_chunk_fwd_stage_name(i).decode() for i in range(nst)]
+    if args.entry == "recurrent":
+        return bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip)
 
     for _ in range(args.warmup):
         rc = lib.kda_chunk_fwd(ctypes.byref(desc), *args_)

@@ -83,7 +83,11 @@ LONG_BF16 = Workload(
     g_dtype=torch.float32, beta_dtype=torch.bfloat16, seed=4, qk_l2norm=True, beta_sigmoid=True,
     allow_neg_eigval=True, pregated_softplus=True)
 
-WORKLOADS = {w.name: w for w in (TINY_FP32, TRAINING_BF16, GVA_BF16, VARLEN_BF16, LONG_BF16)}
+# one decoding step of 64 sequences with the metric configuration's heads: the state of
+# every (sequence, value head) is read and written once (the token-by-token entry)
+DECODE_BF16 = GVA_BF16.replace(name="decode_bf16", B=64, T=1, seed=5)
+
+WORKLOADS = {w.name: w for w in (TINY_FP32, TRAINING_BF16, GVA_BF16, VARLEN_BF16, LONG_BF16, DECODE_BF16)}
 
 
 def _normal(gen, shape, std=1.0):
