@@ -433,18 +433,23 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
             }
         }
     }
-    // KgT staging -> global (each 16-byte unit u sits at element 8u of the fragment-major layout)
-    for (int u = threadIdx.x; u < K * C / 8; u += blockDim.x) {
-        const int tile = u >> 6, within = u & 63;
-        const int d = 16 * (tile / (C / 32)) + (within & 15);
+    // KgT staging -> global (each 16-byte unit u sits at element 8u of the fragment-major layout).
+    // K C / 8 units over NB waves of 64 lanes: NKK rounds, unit u = threadIdx.x + round * 64 NB,
+    // i.e. fragment tile w + round * NB, lane l (unrolled, so the addressing folds to constants)
+    static_assert(K * C / 8 == NKK * NB * 64, "KgT units per round");
+#pragma unroll
+    for (int it = 0; it < NKK; ++it) {
+        const int tile = w + it * NB;
+        const int u = tile * 64 + l;
+        const int d = 16 * (tile / (C / 32)) + lr;
         if constexpr (PERM) {
             // lane group g of a unit holds columns 4g..4g+3 and 16+4g..16+4g+3 of its 32-column block
-            const int m0 = 32 * (tile % (C / 32)) + 4 * (within >> 4);
+            const int m0 = 32 * (tile % (C / 32)) + 4 * cg;
             const uint2 a = *reinterpret_cast<const uint2 *>(KST + swz<C>(d, m0));
             const uint2 b = *reinterpret_cast<const uint2 *>(KST + swz<C>(d, m0 + 16));
             *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = make_uint4(a.x, a.y, b.x, b.y);
         } else {
-            const int m0 = 32 * (tile % (C / 32)) + 8 * (within >> 4);
+            const int m0 = 32 * (tile % (C / 32)) + 8 * cg;
             *reinterpret_cast<uint4 *>(KgTg + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(KST + swz<C>(d, m0));
         }
     }
