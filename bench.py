@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "chunk_kda fwd Mtokens/s at HV=32,K=V=128,T=8K; % of MFMA/HBM roofline"
 METRIC_RECURRENT = "fused_recurrent_kda decode Mtokens/s; % of HBM roofline"
+METRIC_STATES = "chunk_kda fwd with intermediate states Mtokens/s; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 
@@ -161,6 +162,53 @@ def bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip):
     return 0
 
 
+def bench_states(args, w, inp, d, desc, args_, stream, lib, hip):
+    """Times kda_chunk_fwd_states (the forward plus the state each chunk starts from)
+    against kda_chunk_fwd on the same inputs, and prints its own JSON line."""
+    import torch
+
+    C = w.chunk
+    nchunks = sum((L + C - 1) // C for L in inp["seq_lens"])
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    hs = torch.empty((nchunks, HV, K, V), dtype=torch.float32, device=d["q"].device)
+    sargs = args_[:11] + (hs.data_ptr(),) + args_[11:]
+
+    def timed(fn, a):
+        for _ in range(args.warmup):
+            assert fn(ctypes.byref(desc), *a) == 0
+        torch.cuda.synchronize()
+        start, end = hip.event(), hip.event()
+        hip.record(start, stream)
+        for _ in range(args.steps):
+            assert fn(ctypes.byref(desc), *a) == 0
+        hip.record(end, stream)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(start, end) / args.steps
+
+    ms = timed(lib.kda_chunk_fwd_states, sargs)
+    ms_plain = timed(lib.kda_chunk_fwd, args_)
+    ntok = B * T
+    state_bytes = nchunks * HV * K * V * 4
+    alg_bytes = algorithmic_bytes(w, inp) + state_bytes
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_STATES, "value": round(ntok / (ms * 1e-3) / 1e6, 3), "unit": "Mtokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V, "chunk": C,
+                   "sequences": len(inp["seq_lens"]), "intermediate_states": nchunks},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "whole call",
+                     "kernel_ms": round(ms, 5)},
+        "path": {"algorithmic_bytes": alg_bytes, "state_bytes": state_bytes,
+                 "ms_per_step_without_states": round(ms_plain, 5)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(w, inp, kw):
     from oracle import oracle_num_threads
     from tests.oracle_adapter import run_oracle
@@ -181,9 +229,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gva_bf16")
-    ap.add_argument("--entry", choices=("chunk", "recurrent"), default="chunk",
+    ap.add_argument("--entry", choices=("chunk", "recurrent", "states"), default="chunk",
                     help="chunk: kda_chunk_fwd (the metric); recurrent: kda_fused_recurrent_fwd, "
-                         "the token-by-token decoding entry (use with --workload decode_bf16)")
+                         "the token-by-token decoding entry (use with --workload decode_bf16); "
+                         "states: kda_chunk_fwd_states, the forward plus the per-chunk states")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (5 times), the known-size "
@@ -259,6 +308,8 @@ def main() -> int:
     names = [lib.kda_chunk_fwd_stage_name(i).decode() for i in range(nst)]
     if args.entry == "recurrent":
         return bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip)
+    if args.entry == "states":
+        return bench_states(args, w, inp, d, desc, args_, stream, lib, hip)
 
     for _ in range(args.warmup):
         rc = lib.kda_chunk_fwd(ctypes.byref(desc), *args_)

@@ -168,16 +168,18 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               allow_neg_eigval: bool = False, *, workspace: Optional[torch.Tensor] = None,
               cp_context=None, state_v_first: bool = False, transpose_state_layout: bool = False,
               return_intermediate_states: bool = False, disable_recompute: bool = False):
-    """KDA forward on the current HIP stream.  Returns (o, final_state or None).
+    """KDA forward on the current HIP stream.  Returns (o, final_state or None), or
+    (o, final_state or None, h) with return_intermediate_states.
 
     q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]; beta [B, T, HV];
-    initial_state / final_state [N, HV, K, V] float32 (N = B, or len(cu_seqlens) - 1).
-    scale defaults to K ** -0.5.  The o dtype is the q/k/v dtype.
+    initial_state / final_state [N, HV, K, V] float32 (N = B, or len(cu_seqlens) - 1),
+    [N, HV, V, K] with state_v_first / transpose_state_layout (the same switch).
+    h: the state each chunk starts from, float32 [B, NT, HV, K, V] (NT = ceil(T / chunk_size)),
+    or [1, total chunks, HV, K, V] with cu_seqlens (chunks restart at every sequence start),
+    in the same state layout.  scale defaults to K ** -0.5.  The o dtype is the q/k/v dtype.
     """
-    _unsupported(cp_context=cp_context is not None, state_v_first=state_v_first,
-                 transpose_state_layout=transpose_state_layout,
-                 return_intermediate_states=return_intermediate_states,
-                 disable_recompute=disable_recompute)
+    _unsupported(cp_context=cp_context is not None, disable_recompute=disable_recompute)
+    transpose = bool(state_v_first or transpose_state_layout)
     lib = library()
     if q.dim() != 4 or v.dim() != 4:
         raise KDAContractError(_abi.STATUS["KDA_ERR_SHAPE"], "q, k, v must be 4-D [B, T, heads, dim]")
@@ -196,9 +198,12 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _check_tensor(dt_bias, "dt_bias", (HV * K,), dev, torch.float32)
     flags = _flags(use_gate_in_kernel, safe_gate, lower_bound, use_qk_l2norm_in_kernel,
                    use_beta_sigmoid_in_kernel, allow_neg_eigval, output_final_state)
+    if transpose:
+        flags |= _abi.TRANSPOSE_STATE
     desc = _Desc(q, v, g, beta, scale, chunk_size, cu_seqlens, lower_bound, flags)
     N = desc.N
-    _check_tensor(initial_state, "initial_state", (N, HV, K, V), dev, torch.float32)
+    sshape = (V, K) if transpose else (K, V)
+    _check_tensor(initial_state, "initial_state", (N, HV) + sshape, dev, torch.float32)
     cu_dev = None
     if cu_seqlens is not None:
         cu_dev = cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
@@ -210,13 +215,26 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if workspace is None:
         workspace = _workspace(dev, stream, nbytes.value)
     o = torch.empty((B, T, HV, V), dtype=q.dtype, device=dev)
-    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
-    rc = lib.kda_chunk_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                           _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
-                           _ptr(ht), _ptr(workspace), workspace.numel(), stream)
+    ht = torch.empty((N, HV) + sshape, dtype=torch.float32, device=dev) if output_final_state else None
+    if not return_intermediate_states:
+        rc = lib.kda_chunk_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
+                               _ptr(ht), _ptr(workspace), workspace.numel(), stream)
+        if rc != _abi.KDA_OK:
+            _raise(rc, lib)
+        return o, ht
+    if desc.cu_host is not None:
+        lens = desc.cu_host[1:] - desc.cu_host[:-1]
+        hshape = (1, int(((lens + chunk_size - 1) // chunk_size).sum()))
+    else:
+        hshape = (B, (T + chunk_size - 1) // chunk_size)
+    h = torch.empty(hshape + (HV,) + sshape, dtype=torch.float32, device=dev)
+    rc = lib.kda_chunk_fwd_states(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
+                                  _ptr(ht), _ptr(h), _ptr(workspace), workspace.numel(), stream)
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
-    return o, ht
+    return o, ht, h
 
 
 def fused_recurrent_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -226,12 +244,14 @@ def fused_recurrent_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
                         use_gate_in_kernel: bool = False, safe_gate: bool = False,
                         lower_bound: Optional[float] = None, A_log: Optional[torch.Tensor] = None,
                         dt_bias: Optional[torch.Tensor] = None, use_beta_sigmoid_in_kernel: bool = False,
-                        allow_neg_eigval: bool = False):
+                        allow_neg_eigval: bool = False, *, state_v_first: bool = False,
+                        transpose_state_layout: bool = False):
     """Token-by-token KDA forward (decoding) on the current HIP stream.
 
     Same arguments, shapes and result as chunk_kda; the state stays on chip for each
     sequence and there is no workspace.  Returns (o, final_state or None).
     """
+    transpose = bool(state_v_first or transpose_state_layout)
     lib = library()
     if q.dim() != 4 or v.dim() != 4:
         raise KDAContractError(_abi.STATUS["KDA_ERR_SHAPE"], "q, k, v must be 4-D [B, T, heads, dim]")
@@ -250,15 +270,18 @@ def fused_recurrent_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     _check_tensor(dt_bias, "dt_bias", (HV * K,), dev, torch.float32)
     flags = _flags(use_gate_in_kernel, safe_gate, lower_bound, use_qk_l2norm_in_kernel,
                    use_beta_sigmoid_in_kernel, allow_neg_eigval, output_final_state)
+    if transpose:
+        flags |= _abi.TRANSPOSE_STATE
     desc = _Desc(q, v, g, beta, scale, 64, cu_seqlens, lower_bound, flags)
     N = desc.N
-    _check_tensor(initial_state, "initial_state", (N, HV, K, V), dev, torch.float32)
+    sshape = (V, K) if transpose else (K, V)
+    _check_tensor(initial_state, "initial_state", (N, HV) + sshape, dev, torch.float32)
     cu_dev = None
     if cu_seqlens is not None:
         cu_dev = cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
     stream = torch.cuda.current_stream(dev).cuda_stream
     o = torch.empty((B, T, HV, V), dtype=q.dtype, device=dev)
-    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ht = torch.empty((N, HV) + sshape, dtype=torch.float32, device=dev) if output_final_state else None
     rc = lib.kda_fused_recurrent_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                      _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
                                      _ptr(ht), stream)

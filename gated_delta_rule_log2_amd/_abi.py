@@ -26,12 +26,13 @@ QK_L2NORM = 1 << 3
 BETA_SIGMOID = 1 << 4
 ALLOW_NEG_EIGVAL = 1 << 5
 OUTPUT_FINAL_STATE = 1 << 6
+TRANSPOSE_STATE = 1 << 7
 
 # every function include/kda.h declares
 EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
     "kda_gate_chunk_cumsum_workspace_size", "kda_gate_chunk_cumsum", "kda_chunk_fwd_stage_count",
-    "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd",
+    "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd", "kda_chunk_fwd_states",
 )
 
 
@@ -77,6 +78,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
+    lib.kda_chunk_fwd_states.restype = ctypes.c_int
+    lib.kda_chunk_fwd_states.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _vp]
     lib.kda_chunk_fwd_profiled.restype = ctypes.c_int
     lib.kda_chunk_fwd_profiled.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp, _vp]

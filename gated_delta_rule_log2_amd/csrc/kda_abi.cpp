@@ -71,7 +71,7 @@ static kda_status check_desc(const kda_fwd_desc *d, Params &p) {
         return KDA_ERR_UNSUPPORTED;  // fp32 inputs with K = V = 256 exceed one CU's LDS
     if (d->HV % d->H != 0) return KDA_ERR_GVA;
     const uint32_t f = d->flags;
-    if (f & ~0x7fu) return KDA_ERR_UNSUPPORTED;
+    if (f & ~0xffu) return KDA_ERR_UNSUPPORTED;
     const bool has_lb = f & KDA_HAS_LOWER_BOUND;
     const float lb = d->lower_bound;
     if ((f & KDA_SAFE_GATE) && (!has_lb || !(lb >= -5.f && lb < 0.f))) return KDA_ERR_LOWER_BOUND;
@@ -110,6 +110,7 @@ static kda_status check_desc(const kda_fwd_desc *d, Params &p) {
     p.scale = d->scale;
     p.lower_bound_log2 = has_lb ? lb * 1.4426950408889634f : 0.f;
     p.output_final_state = (f & KDA_OUTPUT_FINAL_STATE) ? 1 : 0;
+    p.state_vk = (f & KDA_TRANSPOSE_STATE) ? 1 : 0;
     return KDA_OK;
 }
 
@@ -168,14 +169,20 @@ int kda_chunk_fwd_stage_count(void) { return kNumStages; }
 
 const char *kda_chunk_fwd_stage_name(int i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr; }
 
-kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
-                                  const void *g, const void *beta, const float *A_log, const float *dt_bias,
-                                  const float *initial_state, const int64_t *cu_seqlens, void *o,
-                                  float *final_state, void *workspace, size_t workspace_bytes,
-                                  hipStream_t stream, hipEvent_t *ev) {
+}  // extern "C"
+
+// The whole forward: checks, then plan -> intra -> recurrence on `stream`.  `states`
+// (the state each chunk starts from) is written when want_states; `ev` as for
+// kda_chunk_fwd_profiled.
+static kda_status chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                            const int64_t *cu_seqlens, void *o, float *final_state, bool want_states,
+                            float *states, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                            hipEvent_t *ev) {
     Params p;
     kda_status st = check_desc(d, p);
     if (st != KDA_OK) return st;
+    if (want_states && p.total_chunks > 0 && !states) return KDA_ERR_NULL_POINTER;
     const bool tokens = (int64_t)d->B * d->T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
     if ((d->flags & KDA_OUTPUT_FINAL_STATE) && !final_state) return KDA_ERR_NULL_POINTER;
@@ -189,6 +196,7 @@ kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const vo
     p.A_log = A_log; p.dt_bias = dt_bias; p.h0 = initial_state;
     p.cu_seqlens = cu_seqlens;
     p.o = o; p.ht = final_state;
+    p.hs = want_states ? states : nullptr;
     bind_workspace(p, workspace, L);
 
     hipError_t (*const stages[kNumStages])(const Params &, hipStream_t) = {launch_plan, launch_intra,
@@ -202,13 +210,33 @@ kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const vo
     return to_status(e);
 }
 
+extern "C" {
+
+kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta, const float *A_log, const float *dt_bias,
+                                  const float *initial_state, const int64_t *cu_seqlens, void *o,
+                                  float *final_state, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream, hipEvent_t *ev) {
+    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
+                     nullptr, workspace, workspace_bytes, stream, ev);
+}
+
 kda_status kda_chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
                          const void *g, const void *beta, const float *A_log, const float *dt_bias,
                          const float *initial_state, const int64_t *cu_seqlens, void *o,
                          float *final_state, void *workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-    return kda_chunk_fwd_profiled(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o,
-                                  final_state, workspace, workspace_bytes, stream, nullptr);
+    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
+                     nullptr, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_fwd_states(const kda_fwd_desc *d, const void *q, const void *k, const void *v,
+                                const void *g, const void *beta, const float *A_log, const float *dt_bias,
+                                const float *initial_state, const int64_t *cu_seqlens, void *o,
+                                float *final_state, float *states, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, true,
+                     states, workspace, workspace_bytes, stream, nullptr);
 }
 
 kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v,

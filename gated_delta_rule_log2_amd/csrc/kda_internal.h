@@ -23,6 +23,7 @@ struct Params {
     float scale;
     float lower_bound_log2;        // lower_bound * log2(e): the bounded gate directly in log2 units
     int32_t output_final_state;
+    int32_t state_vk;              // state tensors stored [V][K] (else [K][V]) per (sequence, head)
     // inputs
     const void *q, *k, *v, *g, *beta;
     const float *A_log, *dt_bias, *h0;
@@ -30,6 +31,7 @@ struct Params {
     // outputs
     void *o;
     float *ht;
+    float *hs;                     // [total_chunks, HV, K, V] state each chunk starts from, or nullptr
     float *g_act, *g_cum;          // gate-only entry point
     // workspace
     int32_t *chunk_off;            // [N + 1] first global chunk of each sequence

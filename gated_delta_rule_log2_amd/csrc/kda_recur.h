@@ -296,7 +296,9 @@ __device__ __forceinline__ void chunk_loop(const Params &p, int c0, int c1, int 
     }
 }
 
-template <int C, typename T, int NKK>
+// HS: also write the state each chunk starts from (p.hs); a separate instantiation so
+// the stores add no register pressure to the plain forward.
+template <int C, typename T, int NKK, bool HS>
 __global__ void __launch_bounds__(512) recur_kernel(Params p) {
     using G = Geo<C, T, NKK>;
     constexpr int NRT = G::NRT, K = G::K;
@@ -328,6 +330,8 @@ __global__ void __launch_bounds__(512) recur_kernel(Params p) {
     if (state_role) {
         f32x4 S[NRT][2];
         const size_t sbase = ((size_t)n * p.HV + hv) * K * V;
+        // offset of state element (key row, value column) in a [K][V] or [V][K] state
+        auto sidx = [&](int row, int c) { return p.state_vk ? (size_t)c * K + row : (size_t)row * V + c; };
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             const int t = w + 4 * rt;
@@ -337,11 +341,36 @@ __global__ void __launch_bounds__(512) recur_kernel(Params p) {
                 if (G::has_tile(t) && p.h0) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
-                        S[rt][nt][jj] = p.h0[sbase + (size_t)(16 * t + 4 * cg + jj) * V + v0 + 16 * nt + lr];
+                        S[rt][nt][jj] = p.h0[sbase + sidx(16 * t + 4 * cg + jj, v0 + 16 * nt + lr)];
                 }
             }
         }
-        auto step = [&](const StateOps<C, T, NKK> &op, int) { state_step<C, T, NKK>(op, S, x); };
+        // intermediate-state output: a per-chunk uniform base plus this lane's offset (rows
+        // 4cg.., column v0 + lr), fixed for the kernel
+        const uint32_t hs_lane = p.state_vk ? (uint32_t)(v0 + lr) * K + 4 * cg : (uint32_t)(4 * cg) * V + v0 + lr;
+        auto step = [&](const StateOps<C, T, NKK> &op, int g) {
+            if constexpr (HS) {  // the state chunk g starts from
+                float *hb = p.hs + ((size_t)g * p.HV + hv) * K * V;
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) {
+                    const int t = w + 4 * rt;
+                    if (G::has_tile(t)) {
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt) {
+                            if (p.state_vk) {
+                                *reinterpret_cast<float4 *>(hb + (size_t)(16 * nt) * K + 16 * t + hs_lane) =
+                                    make_float4(S[rt][nt][0], S[rt][nt][1], S[rt][nt][2], S[rt][nt][3]);
+                            } else {
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    (hb + (size_t)(16 * t + jj) * V + 16 * nt)[hs_lane] = S[rt][nt][jj];
+                            }
+                        }
+                    }
+                }
+            }
+            state_step<C, T, NKK>(op, S, x);
+        };
         chunk_loop<kStages, StateOps<C, T, NKK>>(p, c0, c1, hv, w, lr, cg, v0, row_wave, step, step);
         if (p.output_final_state) {
 #pragma unroll
@@ -352,7 +381,7 @@ __global__ void __launch_bounds__(512) recur_kernel(Params p) {
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            p.ht[sbase + (size_t)(16 * t + 4 * cg + jj) * V + v0 + 16 * nt + lr] = S[rt][nt][jj];
+                            p.ht[sbase + sidx(16 * t + 4 * cg + jj, v0 + 16 * nt + lr)] = S[rt][nt][jj];
                 }
             }
         }
@@ -376,17 +405,24 @@ hipError_t launch_recur_ct(const Params &p, hipStream_t s) {
     const int units = p.N * p.HV;
     const int per_xcd = (units + kXCD - 1) / kXCD;
     const dim3 grid((unsigned)(per_xcd * kXCD * (p.V / kBV)));
+    const bool hs = p.hs != nullptr;
+#define KDA_RECUR_CASE(n)                                                                   \
+    case n:                                                                                 \
+        if (hs) hipLaunchKernelGGL((recur_kernel<C, T, n, true>), grid, dim3(512), lds, s, p);  \
+        else hipLaunchKernelGGL((recur_kernel<C, T, n, false>), grid, dim3(512), lds, s, p);    \
+        break;
     switch (p.K / 32) {
-    case 1: hipLaunchKernelGGL((recur_kernel<C, T, 1>), grid, dim3(512), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((recur_kernel<C, T, 2>), grid, dim3(512), lds, s, p); break;
-    case 3: hipLaunchKernelGGL((recur_kernel<C, T, 3>), grid, dim3(512), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((recur_kernel<C, T, 4>), grid, dim3(512), lds, s, p); break;
-    case 5: hipLaunchKernelGGL((recur_kernel<C, T, 5>), grid, dim3(512), lds, s, p); break;
-    case 6: hipLaunchKernelGGL((recur_kernel<C, T, 6>), grid, dim3(512), lds, s, p); break;
-    case 7: hipLaunchKernelGGL((recur_kernel<C, T, 7>), grid, dim3(512), lds, s, p); break;
-    case 8: hipLaunchKernelGGL((recur_kernel<C, T, 8>), grid, dim3(512), lds, s, p); break;
+        KDA_RECUR_CASE(1)
+        KDA_RECUR_CASE(2)
+        KDA_RECUR_CASE(3)
+        KDA_RECUR_CASE(4)
+        KDA_RECUR_CASE(5)
+        KDA_RECUR_CASE(6)
+        KDA_RECUR_CASE(7)
+        KDA_RECUR_CASE(8)
     default: return hipErrorInvalidValue;
     }
+#undef KDA_RECUR_CASE
     return hipGetLastError();
 }
 

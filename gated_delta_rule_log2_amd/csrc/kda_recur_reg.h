@@ -118,7 +118,9 @@ __device__ __forceinline__ void ring_issue_k(const Params &p, unsigned char *rin
     }
 }
 
-template <int C, int NKK>
+// HS: also write the state each chunk starts from (p.hs); a separate instantiation so
+// the stores add no register pressure to the plain forward.
+template <int C, int NKK, bool HS>
 __global__ void __launch_bounds__(64 * (4 + C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 recur_reg_kernel(Params p) {
     constexpr int K = 32 * NKK;
@@ -156,15 +158,33 @@ recur_reg_kernel(Params p) {
         const int cc = 8 * (lr >> 2) + 4 * j + (lr & 3);
         const int col = v0 + cc;
         const size_t sbase = ((size_t)n * p.HV + hv) * K * V;
+        // offset of state element (key row, this lane's column) in a [K][V] or [V][K] state
+        auto sidx = [&](int row) { return p.state_vk ? (size_t)col * K + row : (size_t)row * V + col; };
         f32x4 S[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             S[t] = zero4();
             if (p.h0) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) S[t][jj] = p.h0[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col];
+                for (int jj = 0; jj < 4; ++jj) S[t][jj] = p.h0[sbase + sidx(16 * t + 4 * cg + jj)];
             }
         }
+        // the state chunk c0 + k starts from, into the intermediate-state output: a per-step
+        // uniform base plus this lane's offset (rows 4cg.., its column), fixed for the kernel
+        const uint32_t hs_lane = p.state_vk ? (uint32_t)col * K + 4 * cg : (uint32_t)(4 * cg) * V + col;
+        auto put_states = [&](int k) {
+            float *hb = p.hs + ((size_t)(c0 + k) * p.HV + hv) * K * V;
+            if (p.state_vk) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)  // rows 16t + 4cg .. +3 are contiguous in [V][K]
+                    *reinterpret_cast<float4 *>(hb + hs_lane + 16 * t) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) (hb + (size_t)(16 * t + jj) * V)[hs_lane] = S[t][jj];
+            }
+        };
         // one step's ring operands in registers
         struct Ops {
             uint4 w[NMT][NKK], kg[NT][NMS];
@@ -210,6 +230,7 @@ recur_reg_kernel(Params p) {
         auto step = [&](int k, auto next_tag) {
             constexpr bool has_next = decltype(next_tag)::value;
             uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
+            if constexpr (HS) put_states(k);
             // S in bf16 as the contraction operand (permuted order), handed to the output waves
             uint4 Sb[NKK];
 #pragma unroll
@@ -279,7 +300,7 @@ recur_reg_kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) p.ht[sbase + (size_t)(16 * t + 4 * cg + jj) * V + col] = S[t][jj];
+                for (int jj = 0; jj < 4; ++jj) p.ht[sbase + sidx(16 * t + 4 * cg + jj)] = S[t][jj];
         }
     } else if (!is_loader) {
         // ------------------------------------------------------------ output wave o
@@ -403,11 +424,12 @@ hipError_t launch_recur_reg(const Params &p, hipStream_t s) {
         hipLaunchKernelGGL(kern, grid, dim3(64 * (4 + C / 16)), lds, s, p);
         e = hipGetLastError();
     };
+    const bool hs = p.hs != nullptr;
     switch (p.K / 32) {
-    case 1: go(recur_reg_kernel<C, 1>, RegRecur<C, 32>::kBytes); break;
-    case 2: go(recur_reg_kernel<C, 2>, RegRecur<C, 64>::kBytes); break;
-    case 3: go(recur_reg_kernel<C, 3>, RegRecur<C, 96>::kBytes); break;
-    case 4: go(recur_reg_kernel<C, 4>, RegRecur<C, 128>::kBytes); break;
+    case 1: go(hs ? recur_reg_kernel<C, 1, true> : recur_reg_kernel<C, 1, false>, RegRecur<C, 32>::kBytes); break;
+    case 2: go(hs ? recur_reg_kernel<C, 2, true> : recur_reg_kernel<C, 2, false>, RegRecur<C, 64>::kBytes); break;
+    case 3: go(hs ? recur_reg_kernel<C, 3, true> : recur_reg_kernel<C, 3, false>, RegRecur<C, 96>::kBytes); break;
+    case 4: go(hs ? recur_reg_kernel<C, 4, true> : recur_reg_kernel<C, 4, false>, RegRecur<C, 128>::kBytes); break;
     default: return hipErrorInvalidValue;
     }
     return e;

@@ -48,9 +48,11 @@ __global__ void __launch_bounds__(kRecThreads) fused_recurrent_kernel(Params p) 
     const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[n + 1] : s0 + p.T;
 
     float S[RPT];
-    const size_t sbase = ((size_t)n * p.HV + hv) * K * V + v0 + c;
+    // element (key row d, value column v0 + c) of this unit's state, [K][V] or [V][K]
+    const size_t sbase = ((size_t)n * p.HV + hv) * K * V;
+    auto sidx = [&](int d) { return sbase + (p.state_vk ? (size_t)(v0 + c) * K + d : (size_t)d * V + v0 + c); };
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = p.h0 ? p.h0[sbase + (size_t)(d0 + i) * V] : 0.f;
+    for (int i = 0; i < RPT; ++i) S[i] = p.h0 ? p.h0[sidx(d0 + i)] : 0.f;
 
     const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
     const float lb = p.lower_bound_log2 / kLog2e;  // natural-log lower bound
@@ -133,7 +135,7 @@ __global__ void __launch_bounds__(kRecThreads) fused_recurrent_kernel(Params p) 
     }
     if (p.output_final_state) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) p.ht[sbase + (size_t)(d0 + i) * V] = S[i];
+        for (int i = 0; i < RPT; ++i) p.ht[sidx(d0 + i)] = S[i];
     }
 }
 

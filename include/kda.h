@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -78,7 +78,9 @@ enum {
     KDA_QK_L2NORM = 1u << 3,          /* q, k are L2-normalised per (token, head) in the kernel */
     KDA_BETA_SIGMOID = 1u << 4,       /* beta holds logits; b = sigmoid(beta) */
     KDA_ALLOW_NEG_EIGVAL = 1u << 5,   /* with BETA_SIGMOID: b = 2 * sigmoid(beta), in [0, 2) */
-    KDA_OUTPUT_FINAL_STATE = 1u << 6  /* write final_state */
+    KDA_OUTPUT_FINAL_STATE = 1u << 6, /* write final_state */
+    KDA_TRANSPOSE_STATE = 1u << 7     /* every state tensor stored [V][K] per (sequence, value head)
+                                         instead of [K][V] ("state_v_first", [ENG] §2.2) */
 };
 
 /*
@@ -132,6 +134,7 @@ kda_status kda_chunk_fwd_workspace_size(const kda_fwd_desc *d, size_t *bytes);
  *               optional with a lower bound, NULL meaning exp(A_log) = 1)
  *   dt_bias     [HV * K] fp32 or NULL (0), added to g before the activation
  *   initial_state [num_seqs, HV, K, V] fp32 or NULL (zeros); state rows are keys
+ *               ([num_seqs, HV, V, K] with KDA_TRANSPOSE_STATE, as final_state)
  *   cu_seqlens  [num_seqs + 1] int64 device copy of the packed offsets, or NULL
  *   o           [B, T, HV, V]  qkv_dtype, fully overwritten
  *   final_state [num_seqs, HV, K, V] fp32, written iff KDA_OUTPUT_FINAL_STATE
@@ -149,6 +152,30 @@ kda_status kda_chunk_fwd(const kda_fwd_desc *d,
                          const float *initial_state, const int64_t *cu_seqlens,
                          void *o, float *final_state,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd that also returns the intermediate states: the state each chunk
+ * starts from, for every sequence and value head (the inference-only
+ * "return_intermediate_states" of [ENG] §2.2, the h of [NOTES] forward step 4,
+ * S_[t-1] before the chunk's update), for serving engines that keep per-chunk
+ * states.
+ *   states      [total_chunks, HV, K, V] fp32 ([.., V, K] with KDA_TRANSPOSE_STATE),
+ *               fully overwritten.  Chunks start at every sequence start and then
+ *               every chunk_size tokens; sequence n's chunks follow those of
+ *               sequences 0..n-1, so total_chunks = sum over sequences of
+ *               ceil(length / chunk_size) (B * ceil(T / chunk_size) without
+ *               cu_seqlens).  A sequence's first entry is its initial state (or
+ *               zeros); a sequence of length 0 has none.
+ * Everything else (arguments, workspace, checks, errors) is that of kda_chunk_fwd,
+ * plus KDA_ERR_NULL_POINTER when states is NULL and there are chunks.  o and
+ * final_state are bit for bit those of kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_states(const kda_fwd_desc *d,
+                                const void *q, const void *k, const void *v, const void *g,
+                                const void *beta, const float *A_log, const float *dt_bias,
+                                const float *initial_state, const int64_t *cu_seqlens,
+                                void *o, float *final_state, float *states,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fused_recurrent_kda forward: the token-by-token form of the same operator, the

@@ -87,6 +87,9 @@ typedef struct {
     double lower_bound, scale;
     double *o, *ht;
     const unsigned char *unit_mask; /* [num_seqs * HV], NULL = every unit */
+    int chunk;                      /* snapshot period (tokens), with states */
+    const int64_t *chunk_first;     /* [num_seqs] index of each sequence's first chunk */
+    double *states;                 /* [chunks][HV][K][V] state before each chunk, or NULL */
     int next_unit;                  /* work counter, guarded by lock */
     pthread_mutex_t lock;
 } oracle_job;
@@ -118,6 +121,9 @@ static void run_unit(oracle_job *J, int n, int hv, double *S, double *qv, double
     else memset(S, 0, KV * sizeof(double));
 
     for (int64_t t = J->seq_starts[n]; t < J->seq_starts[n + 1]; ++t) {
+        const int64_t r = t - J->seq_starts[n];
+        if (J->states && r % J->chunk == 0)  /* the state the chunk starting here begins from */
+            memcpy(J->states + ((size_t)(J->chunk_first[n] + r / J->chunk) * HV + hv) * KV, S, KV * sizeof(double));
         load_qk(J->q + ((size_t)t * H + h) * K, K, J->qk_l2norm, J->scale, qv);
         load_qk(J->k + ((size_t)t * H + h) * K, K, J->qk_l2norm, 1.0, kv);
         const double *vt = J->v + ((size_t)t * HV + hv) * V;
@@ -168,6 +174,24 @@ int kda_oracle_num_threads(int requested) {
     return n > 0 ? (int)n : 1;
 }
 
+static int run_job(oracle_job *J, int nthreads) {
+    pthread_mutex_init(&J->lock, NULL);
+    int nt = kda_oracle_num_threads(nthreads);
+    if (nt > J->num_seqs * J->HV) nt = J->num_seqs * J->HV > 0 ? J->num_seqs * J->HV : 1;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+    int failed = 0;
+    for (int i = 0; i < nt; ++i)
+        if (pthread_create(&tid[i], NULL, worker, J) != 0) { nt = i; failed = 1; break; }
+    for (int i = 0; i < nt; ++i) {
+        void *r = NULL;
+        pthread_join(tid[i], &r);
+        if (r) failed = 1;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J->lock);
+    return failed ? -1 : nt;
+}
+
 /*
  * Forward pass.  Shapes (row-major, float64):
  *   q, k [Ttot][H][K];  v [Ttot][HV][V];  g [Ttot][HV][K];  beta [Ttot][HV]
@@ -186,22 +210,29 @@ int kda_oracle_fwd(int num_seqs, const int64_t *seq_starts, int H, int HV, int K
     if (num_seqs < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || HV % H != 0) return -1;
     if (gate_mode == GATE_SOFTPLUS && !A_log) return -1;
     oracle_job J = {num_seqs, seq_starts, H, HV, K, V, q, k, v, g, beta, A_log, dt_bias, h0,
-                    gate_mode, qk_l2norm, beta_mode, lower_bound, scale, o, ht, unit_mask, 0};
-    pthread_mutex_init(&J.lock, NULL);
-    int nt = kda_oracle_num_threads(nthreads);
-    if (nt > num_seqs * HV) nt = num_seqs * HV > 0 ? num_seqs * HV : 1;
-    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
-    int failed = 0;
-    for (int i = 0; i < nt; ++i)
-        if (pthread_create(&tid[i], NULL, worker, &J) != 0) { nt = i; failed = 1; break; }
-    for (int i = 0; i < nt; ++i) {
-        void *r = NULL;
-        pthread_join(tid[i], &r);
-        if (r) failed = 1;
-    }
-    free(tid);
-    pthread_mutex_destroy(&J.lock);
-    return failed ? -1 : nt;
+                    gate_mode, qk_l2norm, beta_mode, lower_bound, scale, o, ht, unit_mask, 0, NULL, NULL, 0};
+    return run_job(&J, nthreads);
+}
+
+/*
+ * kda_oracle_fwd that also records, for every sequence and value head, the state
+ * each chunk starts from: the state after the last token before the chunk (the
+ * sequence's initial state for its first chunk).  Chunks start at every sequence
+ * start and then every `chunk` tokens; sequence n's chunks are numbered from
+ * chunk_first[n].  states: [total chunks][HV][K][V].
+ */
+int kda_oracle_fwd_states(int num_seqs, const int64_t *seq_starts, int H, int HV, int K, int V,
+                          const double *q, const double *k, const double *v, const double *g,
+                          const double *beta, const double *A_log, const double *dt_bias,
+                          int gate_mode, double lower_bound, int qk_l2norm, int beta_mode, double scale,
+                          const double *h0, double *o, double *ht, int chunk, const int64_t *chunk_first,
+                          double *states, int nthreads) {
+    if (num_seqs < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || HV % H != 0) return -1;
+    if (gate_mode == GATE_SOFTPLUS && !A_log) return -1;
+    if (chunk <= 0 || !chunk_first || !states) return -1;
+    oracle_job J = {num_seqs, seq_starts, H, HV, K, V, q, k, v, g, beta, A_log, dt_bias, h0,
+                    gate_mode, qk_l2norm, beta_mode, lower_bound, scale, o, ht, NULL, chunk, chunk_first, states, 0};
+    return run_job(&J, nthreads);
 }
 
 /*

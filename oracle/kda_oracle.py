@@ -50,6 +50,13 @@ def load_oracle(path: str = LIBRARY) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_double,
         _dp, _dp, _dp, _u8p, ctypes.c_int,
     ]
+    lib.kda_oracle_fwd_states.restype = ctypes.c_int
+    lib.kda_oracle_fwd_states.argtypes = [
+        ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+        ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+        _dp, _dp, _dp, ctypes.c_int, _i64p, _dp, ctypes.c_int,
+    ]
     lib.kda_oracle_gate_cumsum.restype = ctypes.c_int
     lib.kda_oracle_gate_cumsum.argtypes = [
         ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -90,12 +97,16 @@ def oracle_num_threads(requested: int = 0, lib_path: str = LIBRARY) -> int:
 def oracle_fwd(q, k, v, g, beta, *, scale: float, gate_mode: int = GATE_PRE,
                lower_bound: float = 0.0, A_log=None, dt_bias=None, qk_l2norm: bool = False,
                beta_mode: int = BETA_AS_GIVEN, initial_state=None, cu_seqlens=None,
-               unit_mask=None, nthreads: int = 0, lib_path: str = LIBRARY):
+               unit_mask=None, nthreads: int = 0, chunk_states: int = 0, lib_path: str = LIBRARY):
     """Token-by-token float64 forward.
 
     q, k: [B, T, H, K]; v: [B, T, HV, V]; g: [B, T, HV, K]; beta: [B, T, HV].
     With cu_seqlens ([N+1], B must be 1) the token axis holds N sequences.
-    Returns (o [B, T, HV, V], ht [N, HV, K, V]) as float64 numpy arrays.
+    Returns (o [B, T, HV, V], ht [N, HV, K, V]) as float64 numpy arrays.  With
+    chunk_states = C > 0 it also returns the state each chunk of C tokens starts
+    from, [total chunks, HV, K, V] (chunks restart at every sequence start;
+    sequence n's chunks follow those of sequences 0..n-1); unit_mask is then not
+    supported.
     """
     q, k, v, g, beta = (_f64(t) for t in (q, k, v, g, beta))
     B, T, H, K = q.shape
@@ -109,12 +120,22 @@ def oracle_fwd(q, k, v, g, beta, *, scale: float, gate_mode: int = GATE_PRE,
     o = np.zeros((B, T, HV, V), np.float64)
     ht = np.zeros((N, HV, K, V), np.float64)
     lib = load_oracle(lib_path)
-    rc = lib.kda_oracle_fwd(
-        N, _ptr(starts, _i64p), H, HV, K, V,
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
-        int(gate_mode), float(lower_bound), int(bool(qk_l2norm)), int(beta_mode), float(scale),
-        _ptr(h0), _ptr(o), _ptr(ht), _ptr(mask, _u8p), int(nthreads),
-    )
+    head = (N, _ptr(starts, _i64p), H, HV, K, V,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+            int(gate_mode), float(lower_bound), int(bool(qk_l2norm)), int(beta_mode), float(scale),
+            _ptr(h0), _ptr(o), _ptr(ht))
+    if chunk_states:
+        if mask is not None:
+            raise ValueError("chunk_states and unit_mask cannot be combined")
+        lens = np.diff(starts)
+        nchunks = (lens + chunk_states - 1) // chunk_states
+        first = np.ascontiguousarray(np.concatenate([[0], np.cumsum(nchunks)[:-1]]).astype(np.int64))
+        states = np.zeros((int(nchunks.sum()), HV, K, V), np.float64)
+        rc = lib.kda_oracle_fwd_states(*head, int(chunk_states), _ptr(first, _i64p), _ptr(states), int(nthreads))
+        if rc < 0:
+            raise ValueError("oracle rejected its arguments")
+        return o, ht, states
+    rc = lib.kda_oracle_fwd(*head, _ptr(mask, _u8p), int(nthreads))
     if rc < 0:
         raise ValueError("oracle rejected its arguments")
     return o, ht

@@ -25,9 +25,10 @@ from __future__ import annotations
 import numpy as np
 
 
-def chunk_form_sequence(q, k, v, g, beta, S0, chunk):
+def chunk_form_sequence(q, k, v, g, beta, S0, chunk, starts_out=None):
     """One sequence, one value head.  q, k, g: [T, K]; v: [T, V]; beta: [T];
-    S0: [K, V].  Returns (o [T, V], S_T [K, V])."""
+    S0: [K, V].  Returns (o [T, V], S_T [K, V]); appends the S each chunk starts
+    from (the S of step 4 before its update) to starts_out when given."""
     T, K = q.shape
     V = v.shape[1]
     S = np.array(S0, dtype=np.float64, copy=True)
@@ -46,6 +47,8 @@ def chunk_form_sequence(q, k, v, g, beta, S0, chunk):
         Qg = np.exp(Gam) * Q
         gC = Gam[-1]
         Kg = np.exp(gC[None, :] - Gam) * Kc
+        if starts_out is not None:
+            starts_out.append(S.copy())
         Vn = U - W @ S                                         # step 4
         o[s:e] = Qg @ S + Aqk @ Vn                             # step 5 (old S)
         S = np.exp(gC)[:, None] * S + Kg.T @ Vn

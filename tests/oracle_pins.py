@@ -29,7 +29,7 @@ from oracle import (
     BETA_AS_GIVEN, BETA_SIGMOID, BETA_TWO_SIGMOID, GATE_LOWER_BOUND, GATE_PRE, GATE_SOFTPLUS,
     oracle_fwd, oracle_gate_cumsum,
 )
-from tests.chunk_form import chunk_form
+from tests.chunk_form import chunk_form, chunk_form_sequence
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -77,6 +77,47 @@ def check_chunk_form(lib):
     # several packed sequences of ragged length, beta up to 2, chunk 32 and 64
     _chunk_case(lib, 3, [70, 5, 33], 1, 2, 4, 4, 32, 2.0, -0.1, True)
     _chunk_case(lib, 4, [130], 2, 2, 4, 3, 64, 1.0, -0.05, True)
+
+
+def _chunk_states_case(lib, seed, lens, H, HV, K, V, chunk):
+    r = _rng(seed)
+    Ttot = int(sum(lens))
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = _unit_rows(r.standard_normal((1, Ttot, H, K)))
+    k = _unit_rows(r.standard_normal((1, Ttot, H, K)))
+    v = r.standard_normal((1, Ttot, HV, V))
+    g = r.uniform(-0.3, 0.0, (1, Ttot, HV, K))
+    beta = r.uniform(0.0, 1.5, (1, Ttot, HV))
+    h0 = 0.3 * r.standard_normal((len(lens), HV, K, V))
+    o, ht, states = oracle_fwd(q, k, v, g, beta, scale=1.0, initial_state=h0, cu_seqlens=starts,
+                               chunk_states=chunk, lib_path=lib)
+    o_plain, ht_plain = oracle_fwd(q, k, v, g, beta, scale=1.0, initial_state=h0, cu_seqlens=starts, lib_path=lib)
+    assert np.array_equal(o, o_plain) and np.array_equal(ht, ht_plain), "snapshots changed the forward"
+    group = HV // H
+    ref = []
+    for n in range(len(lens)):
+        a, b = starts[n], starts[n + 1]
+        per_head = []
+        for hv in range(HV):
+            got = []
+            chunk_form_sequence(q[0, a:b, hv // group], k[0, a:b, hv // group], v[0, a:b, hv], g[0, a:b, hv],
+                                beta[0, a:b, hv], h0[n, hv], chunk, got)
+            per_head.append(got)
+        for c in range(len(per_head[0])):
+            ref.append(np.stack([per_head[hv][c] for hv in range(HV)]))
+    ref = np.stack(ref)
+    assert states.shape == ref.shape, f"chunk states shape {states.shape} != {ref.shape}"
+    _close(states, ref, 1e-11, f"chunk states vs chunk form (chunk {chunk}, lens {lens})")
+    first = np.concatenate([[0], np.cumsum([(L + chunk - 1) // chunk for L in lens])[:-1]])
+    for n in range(len(lens)):
+        assert np.array_equal(states[first[n]], h0[n]), f"sequence {n}: first chunk state is not h0"
+
+
+def check_chunk_states(lib):
+    """The state each chunk starts from equals the S of the chunk form's step 4
+    before its update (the initial state for a sequence's first chunk)."""
+    _chunk_states_case(lib, 40, [37, 16, 50], 1, 2, 4, 3, 16)
+    _chunk_states_case(lib, 41, [70, 9], 2, 2, 5, 4, 32)
 
 
 # --------------------------------------------------------------------------------------------
@@ -346,7 +387,7 @@ def check_non_expansive(lib):
 
 
 ALL_CHECKS = [
-    check_chunk_form, check_beta_zero_pure_decay, check_constant_state, check_exact_write,
+    check_chunk_form, check_chunk_states, check_beta_zero_pure_decay, check_constant_state, check_exact_write,
     check_reflected_write, check_single_token, check_hand_worked, check_gate_closed_forms,
     check_gate_range_and_cumsum, check_gate_parameter_layout, check_beta_modes, check_l2norm_and_scale, check_gva_mapping,
     check_varlen_and_carry, check_non_expansive,

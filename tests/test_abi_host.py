@@ -174,8 +174,18 @@ def test_python_shim_rejects_unsupported_keywords():
     from gated_delta_rule_log2_amd import KDAContractError, chunk_kda
 
     x = torch.zeros(1, 4, 1, 32)
-    for kw in (dict(cp_context=object()), dict(state_v_first=True), dict(return_intermediate_states=True),
-               dict(transpose_state_layout=True), dict(disable_recompute=True)):
+    for kw in (dict(cp_context=object()), dict(disable_recompute=True)):
         with pytest.raises(KDAContractError):
             chunk_kda(x, x, x, x, x[..., 0], **kw)
     assert issubclass(KDAContractError, ValueError)
+
+
+def test_transposed_state_flag_and_states_entry_checks(lib):
+    """KDA_TRANSPOSE_STATE passes the descriptor checks (the next bit does not), and
+    kda_chunk_fwd_states refuses a NULL state output before anything is enqueued."""
+    assert _abi.STATUS_NAMES[ws_status(lib, desc(flags=_abi.TRANSPOSE_STATE))[0]] == "KDA_OK"
+    assert _abi.STATUS_NAMES[ws_status(lib, desc(flags=_abi.TRANSPOSE_STATE << 1))[0]] == "KDA_ERR_UNSUPPORTED"
+    d = desc(flags=_abi.TRANSPOSE_STATE)
+    rc = lib.kda_chunk_fwd_states(ctypes.byref(d), *([None] * 13), 0, None)
+    assert _abi.STATUS_NAMES[rc] == "KDA_ERR_NULL_POINTER"
+

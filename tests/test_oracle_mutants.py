@@ -34,6 +34,8 @@ MUTANTS = [
     ("sigmoid beta ignored", "if (mode == BETA_SIGMOID) return sigmoid(b);", "if (mode == BETA_SIGMOID) return b;"),
     ("no l2 normalisation", "inv = 1.0 / sqrt(ss + 1e-6);", "inv = 1.0;"),
     ("scale dropped", "load_qk(J->q + ((size_t)t * H + h) * K, K, J->qk_l2norm, J->scale, qv);", "load_qk(J->q + ((size_t)t * H + h) * K, K, J->qk_l2norm, 1.0, qv);"),
+    ("chunk state one token late", "if (J->states && r % J->chunk == 0)", "if (J->states && r % J->chunk == 1 % J->chunk)"),
+    ("chunk state index ignores earlier sequences", "J->chunk_first[n] + r / J->chunk", "r / J->chunk"),
     ("initial state ignored", "if (J->h0) memcpy(S, J->h0", "if (0) memcpy(S, J->h0"),
     ("cumsum not reset", "if ((t - seq_starts[n]) % chunk == 0) run = 0.0;", "if (t == seq_starts[n]) run = 0.0;"),
     ("cumsum exclusive", "run += a;\n                    if (g_act) g_act[idx] = a;\n                    g_cum[idx] = run;",
