@@ -143,3 +143,36 @@ def test_intermediate_states_full_size_sampled_heads():
     heads = [3, 30]
     _, _, st_ref = run_oracle(inp, kw, heads=heads, chunk_states=w.chunk)
     check_close("gva_bf16 intermediate states, heads 3 and 30", h[0][:, heads], st_ref, False)
+
+
+def test_intermediate_states_edges():
+    """Empty and chunk-aligned packed segments, and T = 0: a sequence contributes
+    ceil(len / chunk) states (none when empty)."""
+    w = GVA_BF16.replace(name="states_edges", H=1, HV=2, h0="normal0.1")
+    lens = [0, 64, 1, 65, 0, 128, 17]
+    inp = make_inputs(w.replace(T=sum(lens)))
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64)
+    inp["initial_state"] = 0.1 * torch.randn(len(lens), 2, 128, 128, generator=torch.Generator().manual_seed(7))
+    inp["seq_lens"] = lens
+    kw = kernel_kwargs(w)
+    d = to_dev(inp)
+    o, ht, h = call(chunk_kda, d, kw, initial_state=d["initial_state"], return_intermediate_states=True)
+    nch = [(L + 63) // 64 for L in lens]
+    assert h.shape == (1, sum(nch), 2, 128, 128)
+    _, ht_ref, st_ref = run_oracle(inp, kw, chunk_states=64)
+    check_close("states_edges intermediate states", h[0], st_ref, False)
+    check_close("states_edges final state", ht, ht_ref, False)
+    first = np.concatenate([[0], np.cumsum(nch)[:-1]]).astype(int)
+    for n, L in enumerate(lens):
+        if L:
+            assert torch.equal(h[0, first[n]], d["initial_state"][n])
+        else:
+            assert torch.equal(ht[n], d["initial_state"][n]), "empty segment must keep its state"
+    # T = 0: no chunk, no state
+    w0 = GVA_BF16.replace(name="T0", H=1, HV=2, T=0, h0="normal0.1")
+    inp0 = make_inputs(w0)
+    d0 = to_dev(inp0)
+    o0, ht0, h0 = call(chunk_kda, d0, kernel_kwargs(w0), initial_state=d0["initial_state"],
+                       return_intermediate_states=True)
+    assert h0.shape == (1, 0, 2, 128, 128) and o0.shape[1] == 0
+    assert torch.equal(ht0, d0["initial_state"])
