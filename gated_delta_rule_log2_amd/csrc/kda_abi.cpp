@@ -28,6 +28,8 @@ WorkspaceLayout workspace_layout(int32_t N, int32_t total_chunks, int32_t HV, in
     off = align256(off + sizeof(int32_t) * ((size_t)N + 1));
     L.off_chunk_seq = off;
     off = align256(off + sizeof(int32_t) * (size_t)(total_chunks > 0 ? total_chunks : 1));
+    L.off_seq_order = off;
+    off = align256(off + sizeof(int32_t) * ((size_t)N + 1));
     L.plan_bytes = off;
     const size_t slots = (size_t)total_chunks * (size_t)HV;
     L.off_W = off;
@@ -50,6 +52,7 @@ void bind_workspace(Params &p, void *ws, const WorkspaceLayout &L) {
     unsigned char *b = static_cast<unsigned char *>(ws);
     p.chunk_off = reinterpret_cast<int32_t *>(b + L.off_chunk_off);
     p.chunk_seq = reinterpret_cast<int32_t *>(b + L.off_chunk_seq);
+    p.seq_order = reinterpret_cast<int32_t *>(b + L.off_seq_order);
     p.w_W = b + L.off_W;
     p.w_U = b + L.off_U;
     p.w_KgT = b + L.off_KgT;

@@ -36,13 +36,15 @@ struct Params {
     // workspace
     int32_t *chunk_off;            // [N + 1] first global chunk of each sequence
     int32_t *chunk_seq;            // [total_chunks] sequence of each global chunk
+    int32_t *seq_order;            // [N] sequences longest first (packed batches; the
+                                   // recurrence issues its workgroups in this order)
     void *w_W, *w_U, *w_KgT, *w_Qg, *w_Aqk;  // per (chunk, value head) intermediates
     float *w_d;                               // [total_chunks * HV * K] 2^(chunk gate total)
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
 struct WorkspaceLayout {
-    size_t off_chunk_off, off_chunk_seq, off_W, off_U, off_KgT, off_Qg, off_Aqk, off_d;
+    size_t off_chunk_off, off_chunk_seq, off_seq_order, off_W, off_U, off_KgT, off_Qg, off_Aqk, off_d;
     size_t plan_bytes, total_bytes;
 };
 

@@ -8,9 +8,12 @@
 
 namespace kda {
 
+constexpr int kMaxRankedSeqs = 4096;
+
 // One workgroup of 256 threads: exclusive scan of per-sequence chunk counts into
-// chunk_off[0..N], then the inverse map chunk_seq[gc] = n by binary search.  Only
-// packed (cu_seqlens) batches need it; fixed-length batches compute both inline.
+// chunk_off[0..N], the inverse map chunk_seq[gc] = n by binary search, and the
+// recurrence's issue order seq_order.  Only packed (cu_seqlens) batches need it;
+// fixed-length batches compute the tables inline and keep the batch order.
 __global__ void __launch_bounds__(256) plan_kernel(Params p) {
     __shared__ int warp_tot[4];
     __shared__ int carry_s;
@@ -51,6 +54,22 @@ __global__ void __launch_bounds__(256) plan_kernel(Params p) {
             else hi = mid - 1;
         }
         p.chunk_seq[gc] = lo;
+    }
+    // Issue order of the recurrence: sequences by decreasing length (ties by index), so
+    // the longest chains start first and the short ones fill in behind them.  The rank
+    // of n is the number of sequences that go before it; O(N^2 / 256), so above
+    // kMaxRankedSeqs sequences the order stays the packing order.
+    for (int n = tid; n < p.N; n += 256) {
+        int rank = n;
+        if (p.N <= kMaxRankedSeqs) {
+            const int64_t ln = p.cu_seqlens[n + 1] - p.cu_seqlens[n];
+            rank = 0;
+            for (int m = 0; m < p.N; ++m) {
+                const int64_t lm = p.cu_seqlens[m + 1] - p.cu_seqlens[m];
+                rank += (lm > ln || (lm == ln && m < n)) ? 1 : 0;
+            }
+        }
+        p.seq_order[rank] = n;
     }
 }
 

@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(512) recur_kernel(Params p) {
     const int u = (pos / nvt) * kXCD + xcd;
     const int vt = pos % nvt;
     if (u >= p.N * p.HV) return;
-    const int n = u / p.HV, hv = u % p.HV;
+    const int n = p.cu_seqlens ? p.seq_order[u / p.HV] : u / p.HV, hv = u % p.HV;  // longest first
     const int v0 = kBV * vt;
     const int wid = threadIdx.x >> 6, l = lane_id(), lr = l & 15, cg = l >> 4;
     const bool state_role = wid < 4;

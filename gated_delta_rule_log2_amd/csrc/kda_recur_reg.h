@@ -134,7 +134,7 @@ recur_reg_kernel(Params p) {
     const int xcd = blockIdx.x % kXCD, pos = blockIdx.x / kXCD;
     const int u = (pos / nvt) * kXCD + xcd;
     if (u >= p.N * p.HV) return;
-    const int n = u / p.HV, hv = u % p.HV;
+    const int n = p.cu_seqlens ? p.seq_order[u / p.HV] : u / p.HV, hv = u % p.HV;  // longest first
     const int v0 = kBV * (pos % nvt);
     const int wid = threadIdx.x >> 6, l = lane_id(), lr = l & 15, cg = l >> 4;
     // roles: waves 0, 1 state; 4, 5 loaders; 2, 3 and (C = 64) 6, 7 output
