@@ -241,7 +241,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this operator is benchmarked on a single MI355X "
-              "(value heads shard across GPUs with no communication; see DESIGN.md). "
+              "(value heads shard across GPUs with no communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 

@@ -144,7 +144,7 @@ def _flags(use_gate_in_kernel, safe_gate, lower_bound, use_qk_l2norm_in_kernel,
 def _unsupported(**kw):
     for name, val in kw.items():
         if val:
-            raise KDAContractError(_abi.STATUS["KDA_ERR_UNSUPPORTED"], f"{name} is not supported by this build")
+            raise KDAContractError(_abi.STATUS["KDA_ERR_UNSUPPORTED"], f"{name} is not supported")
 
 
 def workspace_bytes(q, v, g, beta, *, chunk_size=64, cu_seqlens=None, scale=None, **flags) -> int:
