@@ -469,11 +469,14 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     }
     if constexpr (PERM) {
         // columns 16s + 4cg.. of blocks 2m and 2m + 1 are adjacent 8-byte halves of one
-        // 16-byte unit: one full store per block pair
+        // 16-byte unit: one full store per block pair.  Pairs right of the diagonal block
+        // (32m > 16w + 15) are zero and never read by the register-resident recurrence,
+        // which loads only the units at or left of it; they are not written.
 #pragma unroll
         for (int m = 0; m < NB / 2; ++m)
-            *reinterpret_cast<uint4 *>(Aqkg + pfrag_off(r, 32 * m + 4 * cg, C)) =
-                make_uint4(aqp[2 * m].x, aqp[2 * m].y, aqp[2 * m + 1].x, aqp[2 * m + 1].y);
+            if (32 * m <= 16 * w + 15)
+                *reinterpret_cast<uint4 *>(Aqkg + pfrag_off(r, 32 * m + 4 * cg, C)) =
+                    make_uint4(aqp[2 * m].x, aqp[2 * m].y, aqp[2 * m + 1].x, aqp[2 * m + 1].y);
     } else {
 #pragma unroll
         for (int s = 0; s < NB; ++s) *reinterpret_cast<uint2 *>(Aqkg + frag_off(r, 16 * s + 4 * cg, C)) = aqp[s];
