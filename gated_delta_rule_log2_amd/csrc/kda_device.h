@@ -79,6 +79,19 @@ __device__ __forceinline__ void store4(uint16_t *p, float a, float b, float c, f
     *reinterpret_cast<uint2 *>(p) = u;
 }
 
+// 16-byte load / store with the non-temporal hint, for data used exactly once (the gate
+// and value inputs, the output): it keeps them from displacing the per-chunk
+// intermediates that the recurrence reads back from the memory-side cache.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_once(const void *ptr) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(ptr));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store16_once(void *ptr, uint4 x) {
+    const u32x4_nt v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt *>(ptr));
+}
+
 // Scalar load of one element of either storage type.
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf2f(*p); }

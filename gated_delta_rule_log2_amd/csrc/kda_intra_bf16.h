@@ -115,8 +115,20 @@ static __device__ float kda_zero_bias[256];
 template <int K>
 __host__ __device__ constexpr bool permuted_layout() { return K <= 128; }
 
-// GB, BB: gate input, beta stored as bf16 (else fp32)
-template <int C, int NKK, bool GB, bool BB>
+// Gate and value inputs are read exactly once.  When the per-chunk intermediates this
+// kernel writes are about the size of the memory-side cache, reading those inputs with
+// the non-temporal hint keeps them from displacing the intermediates the recurrence
+// reads back next (gva_bf16: recurrence -8 us, this kernel +1.5 us); far larger
+// batches gain nothing and pay the slower hinted loads, so they take plain loads.
+constexpr size_t kOnceLoadMaxIntermediates = size_t(384) << 20;
+template <bool NT>
+__device__ __forceinline__ uint4 load16_input(const void *ptr) {
+    if constexpr (NT) return load16_once(ptr);
+    else return *reinterpret_cast<const uint4 *>(ptr);
+}
+
+// GB, BB: gate input, beta stored as bf16 (else fp32); NT: non-temporal gate/value loads
+template <int C, int NKK, bool GB, bool BB, bool NT>
 __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(Params p) {
     constexpr int NB = C / 16, K = 32 * NKK;
     constexpr bool PERM = permuted_layout<K>();
@@ -187,10 +199,10 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         if constexpr (GB) {
-            graw[kk][0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.g) + grow + 32 * kk);
+            graw[kk][0] = load16_input<NT>(static_cast<const uint16_t *>(p.g) + grow + 32 * kk);
         } else {
-            graw[kk][0] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.g) + grow + 32 * kk);
-            graw[kk][1] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.g) + grow + 32 * kk + 4);
+            graw[kk][0] = load16_input<NT>(static_cast<const float *>(p.g) + grow + 32 * kk);
+            graw[kk][1] = load16_input<NT>(static_cast<const float *>(p.g) + grow + 32 * kk + 4);
         }
     }
     // dt_bias for this lane's 8-column groups (read by both activated-gate forms)
@@ -488,7 +500,7 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
     uint4 vpre[4];
 #pragma unroll
     for (int vk = 0; vk < 4; ++vk)
-        if (vk < nvk) vpre[vk] = *reinterpret_cast<const uint4 *>(vrow + 32 * vk);
+        if (vk < nvk) vpre[vk] = load16_input<NT>(vrow + 32 * vk);
     __syncthreads();  // Akk complete
 
     // ---- step 6: A = (I + Akk0)^-1, fp32 ----
@@ -541,7 +553,7 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 #pragma unroll
     for (int vk = 0; vk < 8; ++vk) {
         if (vk < nvk) {
-            const uint4 vv = vk < 4 ? vpre[vk & 3] : *reinterpret_cast<const uint4 *>(vrow + 32 * vk);
+            const uint4 vv = vk < 4 ? vpre[vk & 3] : load16_input<NT>(vrow + 32 * vk);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const f32x4 t = mma32_bf16(zero4(), vv, hh ? sel1 : sel0);
@@ -623,8 +635,15 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
 template <int C, int NKK>
 hipError_t launch_intra_bf16_t(const Params &p, hipStream_t s) {
     const size_t lds = IntraBf16Lds<C, 32 * NKK>::bytes(p.V);
-    auto kern = p.g_bf16 ? (p.beta_bf16 ? intra_bf16_kernel<C, NKK, true, true> : intra_bf16_kernel<C, NKK, true, false>)
-                         : (p.beta_bf16 ? intra_bf16_kernel<C, NKK, false, true> : intra_bf16_kernel<C, NKK, false, false>);
+    // bytes of intermediates per (chunk, value head): W, U, KgT, Qg, Aqk (bf16) and d (fp32)
+    const size_t slot_bytes = 2 * ((size_t)3 * C * (32 * NKK) + (size_t)C * p.V + (size_t)C * C) + 4 * (32 * NKK);
+    const bool nt = (size_t)p.total_chunks * p.HV * slot_bytes <= kOnceLoadMaxIntermediates;
+    auto pick = [&](auto nt_tag) {
+        constexpr bool T = decltype(nt_tag)::value;
+        return p.g_bf16 ? (p.beta_bf16 ? intra_bf16_kernel<C, NKK, true, true, T> : intra_bf16_kernel<C, NKK, true, false, T>)
+                        : (p.beta_bf16 ? intra_bf16_kernel<C, NKK, false, true, T> : intra_bf16_kernel<C, NKK, false, false, T>);
+    };
+    auto kern = nt ? pick(std::true_type{}) : pick(std::false_type{});
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -348,10 +348,9 @@ recur_reg_kernel(Params p) {
             const int64_t tok0 = sb + (int64_t)k * C;
             const int m = 16 * mt0 + lr;
             if (tok0 + m < se)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.o) + ((tok0 + m) * p.HV + hv) * (int64_t)V + v0 +
-                                           8 * cg) =
-                    make_uint4(pack2(acc[0][0], acc[0][1]), pack2(acc[0][2], acc[0][3]), pack2(acc[1][0], acc[1][1]),
-                               pack2(acc[1][2], acc[1][3]));
+                store16_once(static_cast<uint16_t *>(p.o) + ((tok0 + m) * p.HV + hv) * (int64_t)V + v0 + 8 * cg,
+                             make_uint4(pack2(acc[0][0], acc[0][1]), pack2(acc[0][2], acc[0][3]),
+                                        pack2(acc[1][0], acc[1][1]), pack2(acc[1][2], acc[1][3])));
         };
         // Barrier m, then the output of step m - 1 and the loads of step m + 2 into the
         // buffer that output just released: three steps of Qg/Aqk in flight, so the loads'
