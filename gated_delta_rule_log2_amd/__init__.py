@@ -25,7 +25,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["chunk_kda", "fused_recurrent_kda", "gate_chunk_cumsum", "KDAContractError", "KDARuntimeError",
+__all__ = ["chunk_kda", "chunk_kda_bwd", "fused_recurrent_kda", "gate_chunk_cumsum", "KDAContractError", "KDARuntimeError",
            "workspace_bytes", "library"]
 
 
@@ -235,6 +235,66 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
     return o, ht, h
+
+
+def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                  do: torch.Tensor, dht: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                  initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                  chunk_size: int = 64, use_qk_l2norm_in_kernel: bool = False,
+                  use_gate_in_kernel: bool = False, safe_gate: bool = False,
+                  lower_bound: Optional[float] = None, A_log: Optional[torch.Tensor] = None,
+                  dt_bias: Optional[torch.Tensor] = None, use_beta_sigmoid_in_kernel: bool = False,
+                  allow_neg_eigval: bool = False, *, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of <do, o> + <dht, final_state> for chunk_kda's inputs, on the current
+    HIP stream (the forward is recomputed inside).  Arguments as chunk_kda; do has o's
+    shape and dtype, dht the final state's ([N, HV, K, V] float32) or None.  Returns
+    float32 tensors in a dict: dq, dk, dv, dg, dbeta, and dA_log / dt_bias / dh0 for
+    the inputs given (dh0 always: the gradient at the initial state, zero or given).
+    """
+    lib = library()
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KDARuntimeError(_abi.KDA_ERR_HIP, "chunk_kda_bwd runs on a HIP device; got a CPU tensor")
+    scale = 1.0 / math.sqrt(K) if scale is None else float(scale)
+    _check_tensor(k, "k", (B, T, H, K), dev, q.dtype)
+    _check_tensor(v, "v", (B, T, HV, V), dev, q.dtype)
+    _check_tensor(do, "do", (B, T, HV, V), dev, q.dtype)
+    _check_tensor(g, "g", (B, T, HV, K), dev)
+    _check_tensor(beta, "beta", (B, T, HV), dev)
+    _check_tensor(A_log, "A_log", (HV,), dev, torch.float32)
+    _check_tensor(dt_bias, "dt_bias", (HV * K,), dev, torch.float32)
+    flags = _flags(use_gate_in_kernel, safe_gate, lower_bound, use_qk_l2norm_in_kernel,
+                   use_beta_sigmoid_in_kernel, allow_neg_eigval, False)
+    desc = _Desc(q, v, g, beta, scale, chunk_size, cu_seqlens, lower_bound, flags)
+    N = desc.N
+    _check_tensor(initial_state, "initial_state", (N, HV, K, V), dev, torch.float32)
+    _check_tensor(dht, "dht", (N, HV, K, V), dev, torch.float32)
+    cu_dev = None if cu_seqlens is None else cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
+    nbytes = ctypes.c_size_t(0)
+    rc = lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc.d), ctypes.byref(nbytes))
+    if rc != _abi.KDA_OK:
+        _raise(rc, lib)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if workspace is None:
+        workspace = _workspace(dev, stream, nbytes.value)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
+           "dv": torch.empty((B, T, HV, V), **f32), "dg": torch.empty((B, T, HV, K), **f32),
+           "dbeta": torch.empty((B, T, HV), **f32), "dh0": torch.empty((N, HV, K, V), **f32)}
+    if A_log is not None:
+        out["dA_log"] = torch.empty((HV,), **f32)
+    if dt_bias is not None:
+        out["ddt_bias"] = torch.empty((HV * K,), **f32)
+    rc = lib.kda_chunk_bwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                           _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(do), _ptr(dht),
+                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                           _ptr(out["dbeta"]), _ptr(out.get("dA_log")), _ptr(out.get("ddt_bias")),
+                           _ptr(out["dh0"]), _ptr(workspace), workspace.numel(), stream)
+    if rc != _abi.KDA_OK:
+        _raise(rc, lib)
+    return out
 
 
 def fused_recurrent_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

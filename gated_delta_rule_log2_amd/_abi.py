@@ -33,6 +33,7 @@ EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
     "kda_gate_chunk_cumsum_workspace_size", "kda_gate_chunk_cumsum", "kda_chunk_fwd_stage_count",
     "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd", "kda_chunk_fwd_states",
+    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
 )
 
 
@@ -90,6 +91,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_stage_count.argtypes = []
     lib.kda_chunk_fwd_stage_name.restype = ctypes.c_char_p
     lib.kda_chunk_fwd_stage_name.argtypes = [ctypes.c_int]
+    lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = [dp, szp]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [dp] + [_vp] * 20 + [ctypes.c_size_t, _vp]
     lib.kda_gate_chunk_cumsum.restype = ctypes.c_int
     lib.kda_gate_chunk_cumsum.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     if path == LIBRARY:

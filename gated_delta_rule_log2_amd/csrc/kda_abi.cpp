@@ -13,6 +13,7 @@
 #include <cstring>
 
 #include "../../include/kda.h"
+#include "kda_backward.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -282,6 +283,114 @@ kda_status kda_gate_chunk_cumsum(const kda_fwd_desc *d, const void *g, const flo
     hipError_t e = launch_plan(p, stream);
     if (e == hipSuccess) e = launch_gate_cumsum(p, stream);
     return to_status(e);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BwdLayout {
+    size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, total;
+};
+
+// After the forward's own workspace: the chunk-start states, the forward output (not
+// returned), the per-slice partial sums and the per-workgroup token-state scratch.
+BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
+    BwdLayout L{};
+    const size_t Ttot = (size_t)p.B * p.T, ns = (size_t)p.V / 32, f = sizeof(float);
+    size_t off = align256(fwd_bytes);
+    L.off_states = off;
+    off = align256(off + f * (size_t)p.total_chunks * p.HV * p.K * p.V);
+    L.off_o = off;
+    off = align256(off + (p.qkv_bf16 ? 2 : 4) * Ttot * p.HV * p.V);
+    L.off_pdq = off;
+    off = align256(off + f * ns * Ttot * p.HV * p.K);
+    L.off_pdk = off;
+    off = align256(off + f * ns * Ttot * p.HV * p.K);
+    L.off_pdg = off;
+    off = align256(off + f * ns * Ttot * p.HV * p.K);
+    L.off_pdb = off;
+    off = align256(off + f * ns * Ttot * p.HV);
+    const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
+    L.off_sstate = off;
+    off = align256(off + f * scr);
+    L.off_sw = L.off_sstate + f * ((size_t)p.N * p.HV * ns * p.C * p.K * 32);
+    L.off_da = off;
+    off = align256(off + f * Ttot * p.HV * p.K);
+    L.total = off;
+    return L;
+}
+
+kda_status bwd_check(const kda_fwd_desc *d, Params &p) {
+    kda_status st = check_desc(d, p);
+    if (st != KDA_OK) return st;
+    if (d->flags & KDA_TRANSPOSE_STATE) return KDA_ERR_UNSUPPORTED;  // [K][V] states only
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
+    Params p;
+    kda_status st = bwd_check(d, p);
+    if (st != KDA_OK) return st;
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const size_t fwd = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4).total_bytes;
+    *bytes = bwd_layout(p, fwd).total;
+    return KDA_OK;
+}
+
+kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                         const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk,
+                         float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Params p;
+    kda_status st = bwd_check(d, p);
+    if (st != KDA_OK) return st;
+    const bool tokens = (int64_t)d->B * d->T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
+        return KDA_ERR_MISSING_A_LOG;
+    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    const WorkspaceLayout FL = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4);
+    const BwdLayout L = bwd_layout(p, FL.total_bytes);
+    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *states = reinterpret_cast<float *>(ws + L.off_states);
+
+    // forward with the chunk-start states (its output o is not needed)
+    kda_fwd_desc fd = *d;
+    fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
+    st = chunk_fwd(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
+                   states, workspace, FL.total_bytes, stream, nullptr);
+    if (st != KDA_OK) return st;
+
+    BwdParams b{};
+    b.N = p.N; b.T = p.T; b.H = p.H; b.HV = p.HV; b.K = p.K; b.V = p.V; b.C = p.C;
+    b.Ttot = (int64_t)p.B * p.T;
+    b.gate_mode = p.gate_mode; b.beta_mode = p.beta_mode; b.qk_l2norm = p.qk_l2norm;
+    b.qkv_bf16 = p.qkv_bf16; b.g_bf16 = p.g_bf16; b.beta_bf16 = p.beta_bf16;
+    b.scale = d->scale;
+    b.lower_bound = (d->flags & KDA_HAS_LOWER_BOUND) ? d->lower_bound : 0.f;
+    b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.dout = dout;
+    b.A_log = A_log; b.dt_bias = dt_bias; b.dht = dht; b.cu_seqlens = cu_seqlens; b.states = states;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta;
+    b.dA_log = A_log ? dA_log : nullptr;
+    b.ddt_bias = dt_bias ? ddt_bias : nullptr;
+    b.dh0 = dh0;
+    b.p_dq = reinterpret_cast<float *>(ws + L.off_pdq);
+    b.p_dk = reinterpret_cast<float *>(ws + L.off_pdk);
+    b.p_dg = reinterpret_cast<float *>(ws + L.off_pdg);
+    b.p_db = reinterpret_cast<float *>(ws + L.off_pdb);
+    b.scr_state = reinterpret_cast<float *>(ws + L.off_sstate);
+    b.scr_w = reinterpret_cast<float *>(ws + L.off_sw);
+    b.scr_da = reinterpret_cast<float *>(ws + L.off_da);
+    return to_status(launch_backward(b, stream));
 }
 
 }  // extern "C"

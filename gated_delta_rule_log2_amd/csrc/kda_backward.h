@@ -1,0 +1,33 @@
+// kda_backward.h -- launch parameters of the backward kernels (kda_backward.hip).
+// Not part of the public ABI.
+#pragma once
+
+#include "kda_internal.h"
+
+namespace kda {
+
+struct BwdParams {
+    int32_t N, T, H, HV, K, V, C;   // T: tokens per batch row (fixed-length batches)
+    int64_t Ttot;                   // tokens in all
+    int32_t gate_mode, beta_mode, qk_l2norm;
+    int32_t qkv_bf16, g_bf16, beta_bf16;
+    float scale;
+    float lower_bound;              // natural-log units
+    // inputs
+    const void *q, *k, *v, *g, *beta, *dout;
+    const float *A_log, *dt_bias, *dht;
+    const int64_t *cu_seqlens;      // device offsets or nullptr
+    const float *states;            // [total chunks, HV, K, V] state each chunk starts from
+    // outputs (fp32); dA_log, ddt_bias, dh0 may be nullptr
+    float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt_bias, *dh0;
+    // workspace
+    float *p_dq, *p_dk, *p_dg;      // [V / 32, Ttot, HV, K] per-slice sums over V
+    float *p_db;                    // [V / 32, Ttot, HV]
+    float *scr_state, *scr_w;       // per workgroup: [C, K, 32] token states, [C, 32] w
+    float *scr_da;                  // [Ttot, HV, K] dA_log terms
+};
+
+size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C);
+hipError_t launch_backward(const BwdParams &p, hipStream_t s);
+
+}  // namespace kda

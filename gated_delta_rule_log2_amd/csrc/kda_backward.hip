@@ -1,0 +1,368 @@
+// kda_backward.hip -- gradients of the KDA forward ("Reading Notes: Implementation
+// Notes for KDA in FLA", backward section): dq, dk, dv, dg, dbeta, dA_log, dt_bias and
+// initial-state gradients of L = <do, o> + <dht, final_state>.
+//
+// A first, token-level form.  The forward runs first and keeps the state each chunk
+// starts from (the same kernels as the forward entry, with intermediate states).  Then
+// one workgroup per (sequence, value head, 32-column slice of V) walks its chunks last
+// to first: it recomputes the chunk's token states from the chunk-start state, then
+// takes the reverse token step (per token, with P = Diag(alpha) S_prev, u = P^T k^,
+// w = v - u, S = P + b k^ w^T):
+//   dS += q^ do^T;   dq^ = S do;   c = dS^T k^;   e = b c;   dv = e;   db = w . c;
+//   dk^ = b dS w - P e;   dP = dS - k^ e^T;   dg' = rowsum(dP o P);   dS <- Diag(alpha) dP
+// The sums over V (dq^, dk^, dg', db) are written per slice and added by the finishing
+// kernels in a fixed order, which then apply the chain rules of the L2 norm and scale,
+// the gate activation and the beta transform (sums over a GVA group for q and k, over
+// tokens for dA_log and dt_bias).  Everything is fp32.
+#include <hip/hip_runtime.h>
+
+#include "kda_backward.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kBwdThreads = 256;  // 8 row groups x 32 columns
+constexpr int kSlice = 32;
+
+__device__ __forceinline__ float ldf(const void *p, int64_t i, bool bf) {
+    if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+    return static_cast<const float *>(p)[i];
+}
+
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); }
+
+__device__ __forceinline__ float softplus_f(float x) { return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
+
+// natural-log activated gate (the forward's three contracts)
+__device__ __forceinline__ float gate_nat(const BwdParams &p, int hv, int d, float graw) {
+    if (p.gate_mode == kGatePre) return graw;
+    const float x = graw + (p.dt_bias ? p.dt_bias[(int64_t)hv * p.K + d] : 0.f);
+    if (p.gate_mode == kGateSoftplus) return -expf(p.A_log[hv]) * softplus_f(x);
+    const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
+    return p.lower_bound * sigm(a * x);
+}
+
+__device__ __forceinline__ float beta_val(const BwdParams &p, float b) {
+    if (p.beta_mode == kBetaSigmoid) return sigm(b);
+    if (p.beta_mode == kBetaTwoSigmoid) return 2.f * sigm(b);
+    return b;
+}
+
+// sum over the 32 lanes of a half wave (the 32 columns of one row group)
+__device__ __forceinline__ float half_sum(float x) {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+struct TokenLds {
+    float q[256], k[256], a[256];
+    float red[2][8][kSlice];
+    float wsum[4][2];
+    float b;
+};
+
+// q^, k^, alpha of token t into LDS (threads d < K), b too.  Two barriers.
+__device__ void prep_token(const BwdParams &p, TokenLds &s, int64_t t, int h, int hv) {
+    const int tid = threadIdx.x;
+    float qv = 0.f, kv = 0.f, gp = 0.f;
+    if (tid < p.K) {
+        qv = ldf(p.q, (t * p.H + h) * p.K + tid, p.qkv_bf16);
+        kv = ldf(p.k, (t * p.H + h) * p.K + tid, p.qkv_bf16);
+        gp = gate_nat(p, hv, tid, ldf(p.g, (t * p.HV + hv) * p.K + tid, p.g_bf16));
+    }
+    const float sq = wave_sum(qv * qv), sk = wave_sum(kv * kv);
+    if ((tid & 63) == 0) {
+        s.wsum[tid >> 6][0] = sq;
+        s.wsum[tid >> 6][1] = sk;
+    }
+    __syncthreads();
+    float rq = 1.f, rk = 1.f;
+    if (p.qk_l2norm) {
+        float tq = 0.f, tk = 0.f;
+        for (int i = 0; i < kBwdThreads / 64; ++i) tq += s.wsum[i][0], tk += s.wsum[i][1];
+        rq = 1.f / sqrtf(tq + 1e-6f);
+        rk = 1.f / sqrtf(tk + 1e-6f);
+    }
+    if (tid < p.K) {
+        s.q[tid] = qv * rq * p.scale;
+        s.k[tid] = kv * rk;
+        s.a[tid] = expf(gp);
+    }
+    if (tid == 0) s.b = beta_val(p, ldf(p.beta, t * p.HV + hv, p.beta_bf16));
+    __syncthreads();
+}
+
+template <int NR>
+__global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
+    __shared__ TokenLds s;
+    const int ns = p.V / kSlice;
+    const int slice = blockIdx.x % ns;
+    const int hv = (blockIdx.x / ns) % p.HV;
+    const int n = blockIdx.x / (ns * p.HV);
+    const int h = hv / (p.HV / p.H);
+    const int tid = threadIdx.x, j = tid & (kSlice - 1), rg = tid >> 5;
+    const int col = slice * kSlice + j;
+    const int K = p.K, V = p.V, C = p.C;
+    // rows of this thread: rg + 8 i
+    int64_t t_begin, t_end, first_chunk = 0;
+    if (p.cu_seqlens) {
+        t_begin = p.cu_seqlens[n];
+        t_end = p.cu_seqlens[n + 1];
+        for (int m = 0; m < n; ++m) first_chunk += (p.cu_seqlens[m + 1] - p.cu_seqlens[m] + C - 1) / C;
+    } else {
+        t_begin = (int64_t)n * p.T;
+        t_end = t_begin + p.T;
+        first_chunk = (int64_t)n * ((p.T + C - 1) / C);
+    }
+    const int64_t len = t_end - t_begin;
+    const int nchunks = (int)((len + C - 1) / C);
+    float *sc = p.scr_state + (size_t)blockIdx.x * C * K * kSlice;  // S after each token of a chunk
+    float *sw = p.scr_w + (size_t)blockIdx.x * C * kSlice;          // w of each token of a chunk
+
+    float dS[NR], S0[NR], S[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int r = rg + 8 * i;
+        dS[i] = (p.dht && r < K) ? p.dht[(((int64_t)n * p.HV + hv) * K + r) * V + col] : 0.f;
+    }
+    int red_buf = 0;
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int64_t t1 = t0 + C < t_end ? t0 + C : t_end;
+        const float *hc = p.states + ((size_t)(first_chunk + c) * p.HV + hv) * K * V;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + 8 * i;
+            S0[i] = r < K ? hc[(size_t)r * V + col] : 0.f;
+            S[i] = S0[i];
+        }
+        // forward recompute of the chunk's token states
+        for (int64_t t = t0; t < t1; ++t) {
+            prep_token(p, s, t, h, hv);
+            const float vj = ldf(p.v, (t * p.HV + hv) * V + col, p.qkv_bf16);
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                if (r < K) {
+                    S[i] *= s.a[r];
+                    part += S[i] * s.k[r];
+                }
+            }
+            s.red[red_buf][rg][j] = part;
+            __syncthreads();
+            float u = 0.f;
+            for (int g = 0; g < 8; ++g) u += s.red[red_buf][g][j];
+            red_buf ^= 1;
+            const float w = vj - u;
+            const int tl = (int)(t - t0);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                if (r < K) {
+                    S[i] += s.b * s.k[r] * w;
+                    sc[((size_t)tl * K + r) * kSlice + j] = S[i];
+                }
+            }
+            if (rg == 0) sw[tl * kSlice + j] = w;
+        }
+        __syncthreads();  // this workgroup's scratch writes before its reads
+        // reverse token steps
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            prep_token(p, s, t, h, hv);
+            const int tl = (int)(t - t0);
+            const float doj = ldf(p.dout, (t * p.HV + hv) * V + col, p.qkv_bf16);
+            const float w = sw[tl * kSlice + j];
+            float St[NR], Sp[NR];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                St[i] = r < K ? sc[((size_t)tl * K + r) * kSlice + j] : 0.f;
+                Sp[i] = r < K ? (tl > 0 ? sc[((size_t)(tl - 1) * K + r) * kSlice + j] : S0[i]) : 0.f;
+            }
+            const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;  // per-slice partial row
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                if (r < K) {
+                    dS[i] += s.q[r] * doj;
+                    part += dS[i] * s.k[r];
+                }
+            }
+            // dq^ (rows of this thread), summed over the slice's columns
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                const float x = half_sum(St[i] * doj);
+                if (j == 0 && r < K) p.p_dq[pbase * K + r] = x;
+            }
+            s.red[red_buf][rg][j] = part;
+            __syncthreads();
+            float cj = 0.f;
+            for (int g = 0; g < 8; ++g) cj += s.red[red_buf][g][j];
+            red_buf ^= 1;
+            const float b = s.b;
+            const float e = b * cj;
+            if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
+            const float db = half_sum(w * cj);
+            if (tid == 0) p.p_db[pbase] = db;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + 8 * i;
+                const float a = r < K ? s.a[r] : 0.f;
+                const float P = a * Sp[i];
+                const float dk = half_sum(b * dS[i] * w - P * e);
+                const float dP = dS[i] - (r < K ? s.k[r] : 0.f) * e;
+                const float dgp = half_sum(dP * P);
+                if (j == 0 && r < K) {
+                    p.p_dk[pbase * K + r] = dk;
+                    p.p_dg[pbase * K + r] = dgp;
+                }
+                dS[i] = a * dP;
+            }
+        }
+        __syncthreads();  // scratch reads done before the next chunk overwrites it
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + 8 * i;
+            if (r < K) p.dh0[(((int64_t)n * p.HV + hv) * K + r) * V + col] = dS[i];
+        }
+    }
+}
+
+// dq, dk per (token, qk head): the value heads of the group and the V slices summed,
+// then the scale and L2-norm chain rule.  Block of 256 threads, thread d < K.
+__global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
+    __shared__ float ws[4][4];
+    const int64_t t = blockIdx.x / p.H;
+    const int h = blockIdx.x % p.H, d = threadIdx.x;
+    const int group = p.HV / p.H, ns = p.V / kSlice;
+    float gq = 0.f, gk = 0.f, qv = 0.f, kv = 0.f;
+    if (d < p.K) {
+        for (int jv = 0; jv < group; ++jv)
+            for (int sl = 0; sl < ns; ++sl) {
+                const size_t row = ((size_t)sl * p.Ttot + t) * p.HV + h * group + jv;
+                gq += p.p_dq[row * p.K + d];
+                gk += p.p_dk[row * p.K + d];
+            }
+        qv = ldf(p.q, (t * p.H + h) * p.K + d, p.qkv_bf16);
+        kv = ldf(p.k, (t * p.H + h) * p.K + d, p.qkv_bf16);
+    }
+    float dq = gq * p.scale, dk = gk;
+    if (p.qk_l2norm) {
+        const float r0 = wave_sum(qv * qv), r1 = wave_sum(kv * kv), r2 = wave_sum(qv * gq), r3 = wave_sum(kv * gk);
+        if ((d & 63) == 0) ws[d >> 6][0] = r0, ws[d >> 6][1] = r1, ws[d >> 6][2] = r2, ws[d >> 6][3] = r3;
+        __syncthreads();
+        float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+        for (int i = 0; i < kBwdThreads / 64; ++i) sq += ws[i][0], sk += ws[i][1], qd += ws[i][2], kd += ws[i][3];
+        const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
+        // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
+        dq = p.scale * (rq * gq - rq * rq * rq * qv * qd);
+        dk = rk * gk - rk * rk * rk * kv * kd;
+    }
+    if (d < p.K) {
+        p.dq[(t * p.H + h) * p.K + d] = dq;
+        p.dk[(t * p.H + h) * p.K + d] = dk;
+    }
+}
+
+// dg and the per-element dA_log terms per (token, value head), and dbeta.
+__global__ void __launch_bounds__(kBwdThreads) bwd_gate_kernel(BwdParams p) {
+    const int64_t t = blockIdx.x / p.HV;
+    const int hv = blockIdx.x % p.HV, d = threadIdx.x;
+    const int ns = p.V / kSlice;
+    if (d < p.K) {
+        float gp = 0.f;  // dL/dg' (natural-log activated gate)
+        for (int sl = 0; sl < ns; ++sl) gp += p.p_dg[(((size_t)sl * p.Ttot + t) * p.HV + hv) * p.K + d];
+        const size_t idx = (t * p.HV + hv) * p.K + d;
+        float dg = gp, da = 0.f;
+        if (p.gate_mode != kGatePre) {
+            const float x = ldf(p.g, idx, p.g_bf16) + (p.dt_bias ? p.dt_bias[(int64_t)hv * p.K + d] : 0.f);
+            if (p.gate_mode == kGateSoftplus) {
+                const float ea = expf(p.A_log[hv]);
+                dg = gp * (-ea) * sigm(x);
+                da = gp * (-ea * softplus_f(x));
+            } else {
+                const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
+                const float sg = sigm(a * x);
+                const float ds = p.lower_bound * sg * (1.f - sg);
+                dg = gp * ds * a;
+                da = gp * ds * a * x;
+            }
+        }
+        p.dg[idx] = dg;
+        p.scr_da[idx] = da;
+    }
+    if (d == 0) {
+        float db = 0.f;
+        for (int sl = 0; sl < ns; ++sl) db += p.p_db[((size_t)sl * p.Ttot + t) * p.HV + hv];
+        const float braw = ldf(p.beta, t * p.HV + hv, p.beta_bf16);
+        if (p.beta_mode == kBetaSigmoid) db *= sigm(braw) * (1.f - sigm(braw));
+        else if (p.beta_mode == kBetaTwoSigmoid) db *= 2.f * sigm(braw) * (1.f - sigm(braw));
+        p.dbeta[t * p.HV + hv] = db;
+    }
+}
+
+// dt_bias and A_log gradients: sums over tokens (and channels for A_log), one block
+// per value head, tokens in order.
+__global__ void __launch_bounds__(kBwdThreads) bwd_param_kernel(BwdParams p) {
+    __shared__ float ws[4];
+    const int hv = blockIdx.x, d = threadIdx.x;
+    float sdg = 0.f, sda = 0.f;
+    if (d < p.K)
+        for (int64_t t = 0; t < p.Ttot; ++t) {
+            const size_t idx = (t * p.HV + hv) * p.K + d;
+            sdg += p.dg[idx];
+            sda += p.scr_da[idx];
+        }
+    if (p.ddt_bias && d < p.K) p.ddt_bias[(int64_t)hv * p.K + d] = sdg;
+    const float r = wave_sum(sda);
+    if ((d & 63) == 0) ws[d >> 6] = r;
+    __syncthreads();
+    if (d == 0 && p.dA_log) p.dA_log[hv] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+}  // namespace
+
+size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C) {
+    return (size_t)N * HV * (V / kSlice) * C * ((size_t)K * kSlice + kSlice);
+}
+
+hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
+    const int ns = p.V / kSlice;
+    const unsigned units = (unsigned)p.N * (unsigned)p.HV * (unsigned)ns;
+    if (units > 0) {
+        switch (p.K / 32) {
+        case 1: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(bwd_seq_kernel<8>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 3: hipLaunchKernelGGL(bwd_seq_kernel<12>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 4: hipLaunchKernelGGL(bwd_seq_kernel<16>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 5: hipLaunchKernelGGL(bwd_seq_kernel<20>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 6: hipLaunchKernelGGL(bwd_seq_kernel<24>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 7: hipLaunchKernelGGL(bwd_seq_kernel<28>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 8: hipLaunchKernelGGL(bwd_seq_kernel<32>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (p.Ttot > 0) {
+        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)(p.Ttot * p.H)), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);
+    }
+    if (p.gate_mode != kGatePre) hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

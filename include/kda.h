@@ -200,6 +200,39 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
                                    void *o, float *final_state, hipStream_t stream);
 
 /*
+ * chunk_kda backward: the gradients of L = <do, o> + <dht, final_state> with respect
+ * to every input of kda_chunk_fwd ("Reading Notes: Implementation Notes for KDA in
+ * FLA", backward; the same operator, descriptor and input contract as kda_chunk_fwd).
+ * It runs the forward first (keeping the state each chunk starts from in the
+ * workspace), then walks every (sequence, value head) from its last token to its
+ * first.  A first, token-level form: correct for every configuration the forward
+ * accepts except KDA_TRANSPOSE_STATE (KDA_ERR_UNSUPPORTED), not tuned for speed.
+ *   dout     [B*T, HV, V]  dtype qkv_dtype (the dtype of o); required when B*T > 0
+ *   dht      [N, HV, K, V] fp32 gradient of final_state, or NULL (zero)
+ * Outputs, all fp32, fully overwritten, same layouts as the inputs:
+ *   dq, dk   [B*T, H, K]   (summed over the value heads of each GVA group)
+ *   dv       [B*T, HV, V];  dg [B*T, HV, K] (w.r.t. the g given, natural-log units,
+ *            through the activation when KDA_GATE_IN_KERNEL);  dbeta [B*T, HV]
+ *            (w.r.t. the beta given, through the sigmoid when KDA_BETA_SIGMOID)
+ *   dA_log   [HV]     written when both A_log and dA_log are non-NULL
+ *   ddt_bias [HV, K]  written when both dt_bias and ddt_bias are non-NULL
+ *   dh0      [N, HV, K, V] gradient of the initial state, written when non-NULL
+ *            (also without initial_state: the gradient at a zero initial state)
+ * Workspace: kda_chunk_bwd_workspace_size bytes, device memory owned by the caller,
+ * not retained.  Errors: those of kda_chunk_fwd, KDA_ERR_NULL_POINTER for a missing
+ * dout or required output when B*T > 0.  Asynchronous on `stream`.
+ */
+kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes);
+kda_status kda_chunk_bwd(const kda_fwd_desc *d,
+                         const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const float *A_log, const float *dt_bias,
+                         const float *initial_state, const int64_t *cu_seqlens,
+                         const void *dout, const float *dht,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                         float *dA_log, float *ddt_bias, float *dh0,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stage introspection for profiling.  kda_chunk_fwd enqueues
  * kda_chunk_fwd_stage_count() kernels in order; kda_chunk_fwd_stage_name(i)
  * names stage i (NULL when i is out of range).

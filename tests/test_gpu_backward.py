@@ -1,0 +1,85 @@
+"""Backward of chunk_kda on the GPU against the float64 backward oracle.
+
+Every gradient (dq, dk, dv, dg, dbeta, dA_log, dt_bias, dh0) is compared element by
+element on the same seeded inputs.  Tolerance (relative Frobenius norm of the error):
+1e-3 for fp32 inputs, whose forward states carry fp32 rounding only; 2e-2 for bf16
+inputs, the forward's own bar, since the states the backward starts from come from
+the bf16 chunked forward.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_log2_amd import chunk_kda_bwd
+from gated_delta_rule_log2_amd.workloads import (GVA_BF16, LONG_BF16, TINY_FP32, TRAINING_BF16, VARLEN_BF16, kernel_kwargs,
+                                                make_inputs)
+from oracle.kda_oracle_bwd import oracle_bwd
+from tests.oracle_adapter import oracle_modes, rel_frobenius, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+CASES = [
+    TINY_FP32.replace(name="bwd_tiny_fp32_h0", T=150, h0="normal0.1"),
+    TINY_FP32.replace(name="bwd_fp32_k128_c32", T=97, H=1, HV=2, K=128, V=64, chunk=32),
+    GVA_BF16.replace(name="bwd_gva_bf16", T=200, H=2, HV=4),
+    VARLEN_BF16.replace(name="bwd_varlen_bf16", num_seqs=4, min_len=1, max_len=120, H=1, HV=2, K=64, V=64),
+    TRAINING_BF16.replace(name="bwd_softplus_bf16", T=130, H=1, HV=2, K=64, V=32, safe_gate=False, lower_bound=None),
+    TRAINING_BF16.replace(name="bwd_k256_bf16", T=70, H=1, HV=1, K=256, V=64),
+    LONG_BF16.replace(name="bwd_pregated_negeig", T=100, H=1, HV=2, K=64, V=64),
+]
+
+
+def gpu_grads(inp, kw, do, dht):
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    out = chunk_kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.to(DEV),
+                        dht=None if dht is None else dht.to(DEV), A_log=d["A_log"], dt_bias=d["dt_bias"],
+                        initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_grads(inp, kw, do, dht):
+    gate, bmode = oracle_modes(kw)
+    return oracle_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], do, dht=dht, scale=kw["scale"],
+                      gate_mode=gate, lower_bound=kw.get("lower_bound") or 0.0, A_log=inp.get("A_log"),
+                      dt_bias=inp.get("dt_bias"), qk_l2norm=kw.get("use_qk_l2norm_in_kernel", False),
+                      beta_mode=bmode, initial_state=inp.get("initial_state"), cu_seqlens=inp.get("cu_seqlens"))
+
+
+def cotangents(inp, seed=11):
+    gen = torch.Generator().manual_seed(seed)
+    v = inp["v"]
+    N = len(inp["seq_lens"])
+    HV, K, V = v.shape[2], inp["q"].shape[3], v.shape[3]
+    do = torch.randn(v.shape, generator=gen).to(v.dtype)
+    dht = 0.5 * torch.randn((N, HV, K, V), generator=gen)
+    return do, dht
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_backward_parity(w):
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    kw = kernel_kwargs(w)
+    kw.pop("output_final_state", None)
+    do, dht = cotangents(inp)
+    got = gpu_grads(inp, kw, do, dht)
+    ref = oracle_grads(inp, kw, do, dht)
+    tol = 1e-3 if w.dtype == torch.float32 else 2e-2
+    names = {"dq": "dq", "dk": "dk", "dv": "dv", "dg": "dg", "dbeta": "dbeta", "dh0": "dh0",
+             "dA_log": "dA_log", "ddt_bias": "ddt_bias"}
+    for key, rkey in names.items():
+        if rkey not in ref and key == "dh0":
+            rkey = None
+        if key not in got:
+            continue
+        x = to_np(got[key])
+        assert np.all(np.isfinite(x)), f"{w.name} {key}: non-finite"
+        if rkey is None:  # no initial state given: the oracle has no leaf for it
+            continue
+        r = ref[rkey].reshape(x.shape)
+        e = rel_frobenius(x, r)
+        print(f"{w.name} {key}: rel-Frobenius {e:.3e}", flush=True)
+        assert e <= tol, f"{w.name} {key}: rel-Frobenius {e:.3e} > {tol}"
