@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "chunk_kda fwd Mtokens/s at HV=32,K=V=128,T=8K; % of MFMA/HBM roofline"
 METRIC_RECURRENT = "fused_recurrent_kda decode Mtokens/s; % of HBM roofline"
 METRIC_STATES = "chunk_kda fwd with intermediate states Mtokens/s; % of HBM roofline"
+METRIC_BWD = "chunk_kda backward (forward recomputed inside) Mtokens/s; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 
@@ -209,6 +210,68 @@ def bench_states(args, w, inp, d, desc, args_, stream, lib, hip):
     return 0
 
 
+def bench_bwd(args, w, inp, d, desc, args_, stream, lib, hip):
+    """Times kda_chunk_bwd (the forward with per-chunk states, then the backward
+    kernels) and prints its own JSON line; the forward alone is timed beside it."""
+    import torch
+
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    N = len(inp["seq_lens"])
+    dev = d["q"].device
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    do = torch.randn((B, T, HV, V), generator=gen).to(device=dev, dtype=d["q"].dtype)
+    dht = (0.5 * torch.randn((N, HV, K, V), generator=gen)).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = [torch.empty((B, T, H, K), **f32), torch.empty((B, T, H, K), **f32), torch.empty((B, T, HV, V), **f32),
+            torch.empty((B, T, HV, K), **f32), torch.empty((B, T, HV), **f32),
+            torch.empty((HV,), **f32) if d["A_log"] is not None else None,
+            torch.empty((HV * K,), **f32) if d["dt_bias"] is not None else None, torch.empty((N, HV, K, V), **f32)]
+    nbytes = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)) == 0
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+
+    def p(t):
+        return None if t is None else t.data_ptr()
+
+    bargs = args_[:9] + (p(do), p(dht)) + tuple(p(t) for t in outs) + (p(ws), ws.numel(), stream)
+
+    def timed(fn, a, steps, warmup):
+        for _ in range(warmup):
+            assert fn(ctypes.byref(desc), *a) == 0
+        torch.cuda.synchronize()
+        start, end = hip.event(), hip.event()
+        hip.record(start, stream)
+        for _ in range(steps):
+            assert fn(ctypes.byref(desc), *a) == 0
+        hip.record(end, stream)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(start, end) / steps
+
+    ms = timed(lib.kda_chunk_bwd, bargs, args.steps, min(args.warmup, 2))
+    ms_fwd = timed(lib.kda_chunk_fwd, args_, 20, 5)
+    ntok = B * T
+    eb = d["q"].element_size()
+    # read: the forward's inputs, do and dht; written: the fp32 gradients
+    alg_bytes = (algorithmic_bytes(w, inp) + ntok * HV * V * eb + N * HV * K * V * 4
+                 + 4 * ntok * (2 * H * K + HV * V + HV * K + HV) + 4 * N * HV * K * V)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_BWD, "value": round(ntok / (ms * 1e-3) / 1e6, 3), "unit": "Mtokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": min(args.warmup, 2), "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V, "chunk": w.chunk,
+                   "sequences": N},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "whole call",
+                     "kernel_ms": round(ms, 4)},
+        "path": {"algorithmic_bytes": alg_bytes, "forward_ms": round(ms_fwd, 5)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(w, inp, kw):
     from oracle import oracle_num_threads
     from tests.oracle_adapter import run_oracle
@@ -229,10 +292,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gva_bf16")
-    ap.add_argument("--entry", choices=("chunk", "recurrent", "states"), default="chunk",
+    ap.add_argument("--entry", choices=("chunk", "recurrent", "states", "bwd"), default="chunk",
                     help="chunk: kda_chunk_fwd (the metric); recurrent: kda_fused_recurrent_fwd, "
                          "the token-by-token decoding entry (use with --workload decode_bf16); "
-                         "states: kda_chunk_fwd_states, the forward plus the per-chunk states")
+                         "states: kda_chunk_fwd_states, the forward plus the per-chunk states; "
+                         "bwd: kda_chunk_bwd, the backward (forward recomputed inside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (5 times), the known-size "
@@ -310,6 +374,8 @@ def main() -> int:
         return bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip)
     if args.entry == "states":
         return bench_states(args, w, inp, d, desc, args_, stream, lib, hip)
+    if args.entry == "bwd":
+        return bench_bwd(args, w, inp, d, desc, args_, stream, lib, hip)
 
     for _ in range(args.warmup):
         rc = lib.kda_chunk_fwd(ctypes.byref(desc), *args_)

@@ -83,3 +83,34 @@ def test_backward_parity(w):
         e = rel_frobenius(x, r)
         print(f"{w.name} {key}: rel-Frobenius {e:.3e}", flush=True)
         assert e <= tol, f"{w.name} {key}: rel-Frobenius {e:.3e} > {tol}"
+
+
+def test_backward_edges():
+    """Empty and chunk-aligned packed segments (an empty one passes dht straight to
+    dh0), and T = 0 (only dh0 = dht)."""
+    w = GVA_BF16.replace(name="bwd_edges", H=1, HV=2, K=64, V=64, h0="normal0.1")
+    lens = [0, 64, 1, 65, 0, 17]
+    inp = make_inputs(w.replace(T=sum(lens)))
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64)
+    inp["initial_state"] = 0.1 * torch.randn(len(lens), 2, 64, 64, generator=torch.Generator().manual_seed(7))
+    inp["seq_lens"] = lens
+    kw = kernel_kwargs(w)
+    kw.pop("output_final_state", None)
+    do, dht = cotangents(inp)
+    got = gpu_grads(inp, kw, do, dht)
+    ref = oracle_grads(inp, kw, do, dht)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0", "dA_log", "ddt_bias"):
+        x = to_np(got[key])
+        e = rel_frobenius(x, ref[key].reshape(x.shape))
+        print(f"bwd_edges {key}: rel-Frobenius {e:.3e}", flush=True)
+        assert e <= 2e-2, f"bwd_edges {key}: rel-Frobenius {e:.3e}"
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(got["dh0"][n].cpu(), dht[n]), "empty segment: dh0 must equal dht"
+    w0 = GVA_BF16.replace(name="bwd_T0", H=1, HV=2, K=64, V=64, T=0, h0="normal0.1")
+    inp0 = make_inputs(w0)
+    kw0 = kernel_kwargs(w0)
+    kw0.pop("output_final_state", None)
+    do0, dht0 = cotangents(inp0)
+    got0 = gpu_grads(inp0, kw0, do0, dht0)
+    assert torch.equal(got0["dh0"].cpu(), dht0) and got0["dq"].shape[1] == 0
