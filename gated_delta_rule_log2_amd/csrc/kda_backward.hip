@@ -34,13 +34,13 @@ __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); 
 
 __device__ __forceinline__ float softplus_f(float x) { return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x)); }
 
-// natural-log activated gate (the forward's three contracts)
-__device__ __forceinline__ float gate_nat(const BwdParams &p, int hv, int d, float graw) {
+// natural-log activated gate (the forward's three contracts); ea = exp(A_log[hv]) (1
+// without A_log) and bias = dt_bias[hv][d] (0 without) are the per-head constants
+__device__ __forceinline__ float gate_nat(const BwdParams &p, float ea, float bias, float graw) {
     if (p.gate_mode == kGatePre) return graw;
-    const float x = graw + (p.dt_bias ? p.dt_bias[(int64_t)hv * p.K + d] : 0.f);
-    if (p.gate_mode == kGateSoftplus) return -expf(p.A_log[hv]) * softplus_f(x);
-    const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
-    return p.lower_bound * sigm(a * x);
+    const float x = graw + bias;
+    if (p.gate_mode == kGateSoftplus) return -ea * softplus_f(x);
+    return p.lower_bound * sigm(ea * x);
 }
 
 __device__ __forceinline__ float beta_val(const BwdParams &p, float b) {
@@ -49,17 +49,30 @@ __device__ __forceinline__ float beta_val(const BwdParams &p, float b) {
     return b;
 }
 
-// sum over the 32 lanes of a half wave (the 32 columns of one row group)
-__device__ __forceinline__ float half_sum(float x) {
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// sum over the 16 lanes of a DPP row, in every lane: quad_perm [1,0,3,2] and [2,3,0,1]
+// add the quad, row_ror 4 and 8 the other quads (every lane of a row stays in its row)
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x128>(x);
     return x;
 }
 
+// sum over the 32 lanes of a half wave (the 32 columns of one row group)
+__device__ __forceinline__ float half_sum(float x) {
+    x = row_sum16(x);
+    return x + __shfl_xor(x, 16, 64);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    return x;
+    x = half_sum(x);
+    return x + __shfl_xor(x, 32, 64);
 }
 
 struct TokenLds {
@@ -69,15 +82,31 @@ struct TokenLds {
     float b;
 };
 
-// q^, k^, alpha of token t into LDS (threads d < K), b too.  Two barriers.
-__device__ void prep_token(const BwdParams &p, TokenLds &s, int64_t t, int h, int hv) {
+// One token's raw inputs for this thread: q, k, g of channel tid (tid < K), beta, and
+// the value-column input (v or do) of this thread's column.  Loaded a token ahead.
+struct TokenRaw {
+    float q, k, g, beta, col;
+};
+
+__device__ __forceinline__ TokenRaw load_token(const BwdParams &p, int64_t t, int h, int hv, int col,
+                                               const void *colsrc) {
+    TokenRaw r{0.f, 0.f, 0.f, 0.f, 0.f};
     const int tid = threadIdx.x;
-    float qv = 0.f, kv = 0.f, gp = 0.f;
     if (tid < p.K) {
-        qv = ldf(p.q, (t * p.H + h) * p.K + tid, p.qkv_bf16);
-        kv = ldf(p.k, (t * p.H + h) * p.K + tid, p.qkv_bf16);
-        gp = gate_nat(p, hv, tid, ldf(p.g, (t * p.HV + hv) * p.K + tid, p.g_bf16));
+        r.q = ldf(p.q, (t * p.H + h) * p.K + tid, p.qkv_bf16);
+        r.k = ldf(p.k, (t * p.H + h) * p.K + tid, p.qkv_bf16);
+        r.g = ldf(p.g, (t * p.HV + hv) * p.K + tid, p.g_bf16);
     }
+    if (tid == 0) r.beta = ldf(p.beta, t * p.HV + hv, p.beta_bf16);
+    r.col = ldf(colsrc, (t * p.HV + hv) * p.V + col, p.qkv_bf16);
+    return r;
+}
+
+// q^, k^, alpha of a token into LDS (threads d < K), b too.  Two barriers.
+__device__ void prep_token(const BwdParams &p, TokenLds &s, const TokenRaw &x, float ea, float bias) {
+    const int tid = threadIdx.x;
+    const float qv = x.q, kv = x.k;
+    const float gp = tid < p.K ? gate_nat(p, ea, bias, x.g) : 0.f;
     const float sq = wave_sum(qv * qv), sk = wave_sum(kv * kv);
     if ((tid & 63) == 0) {
         s.wsum[tid >> 6][0] = sq;
@@ -96,7 +125,7 @@ __device__ void prep_token(const BwdParams &p, TokenLds &s, int64_t t, int h, in
         s.k[tid] = kv * rk;
         s.a[tid] = expf(gp);
     }
-    if (tid == 0) s.b = beta_val(p, ldf(p.beta, t * p.HV + hv, p.beta_bf16));
+    if (tid == 0) s.b = beta_val(p, x.beta);
     __syncthreads();
 }
 
@@ -127,6 +156,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     float *sc = p.scr_state + (size_t)blockIdx.x * C * K * kSlice;  // S after each token of a chunk
     float *sw = p.scr_w + (size_t)blockIdx.x * C * kSlice;          // w of each token of a chunk
 
+    const float ea = p.A_log ? expf(p.A_log[hv]) : 1.f;
+    const float bias = (p.dt_bias && tid < K) ? p.dt_bias[(int64_t)hv * K + tid] : 0.f;
     float dS[NR], S0[NR], S[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -145,9 +176,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
             S[i] = S0[i];
         }
         // forward recompute of the chunk's token states
+        TokenRaw cur = load_token(p, t0, h, hv, col, p.v);
         for (int64_t t = t0; t < t1; ++t) {
-            prep_token(p, s, t, h, hv);
-            const float vj = ldf(p.v, (t * p.HV + hv) * V + col, p.qkv_bf16);
+            const TokenRaw nxt = t + 1 < t1 ? load_token(p, t + 1, h, hv, col, p.v) : cur;
+            prep_token(p, s, cur, ea, bias);
+            const float vj = cur.col;
+            cur = nxt;
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
@@ -176,18 +210,28 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
         }
         __syncthreads();  // this workgroup's scratch writes before its reads
         // reverse token steps
-        for (int64_t t = t1 - 1; t >= t0; --t) {
-            prep_token(p, s, t, h, hv);
-            const int tl = (int)(t - t0);
-            const float doj = ldf(p.dout, (t * p.HV + hv) * V + col, p.qkv_bf16);
-            const float w = sw[tl * kSlice + j];
-            float St[NR], Sp[NR];
+        // saved states of a token: S after it (St) and before it (Sp), and its w
+        auto load_saved = [&](int tl, float (&St)[NR], float (&Sp)[NR], float &w) {
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int r = rg + 8 * i;
-                St[i] = r < K ? sc[((size_t)tl * K + r) * kSlice + j] : 0.f;
-                Sp[i] = r < K ? (tl > 0 ? sc[((size_t)(tl - 1) * K + r) * kSlice + j] : S0[i]) : 0.f;
+                St[i] = sc[((size_t)tl * K + r) * kSlice + j];
+                Sp[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + r) * kSlice + j] : S0[i];
             }
+            w = sw[tl * kSlice + j];
+        };
+        TokenRaw rcur = load_token(p, t1 - 1, h, hv, col, p.dout);
+        float St[NR], Sp[NR], w;
+        load_saved((int)(t1 - 1 - t0), St, Sp, w);
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const int tl = (int)(t - t0);
+            const TokenRaw rnxt = t > t0 ? load_token(p, t - 1, h, hv, col, p.dout) : rcur;
+            float Stn[NR], Spn[NR], wn = w;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) Stn[i] = St[i], Spn[i] = Sp[i];
+            if (t > t0) load_saved(tl - 1, Stn, Spn, wn);
+            prep_token(p, s, rcur, ea, bias);
+            const float doj = rcur.col;
             const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;  // per-slice partial row
             float part = 0.f;
 #pragma unroll
@@ -229,6 +273,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
                 }
                 dS[i] = a * dP;
             }
+            rcur = rnxt;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) St[i] = Stn[i], Sp[i] = Spn[i];
+            w = wn;
         }
         __syncthreads();  // scratch reads done before the next chunk overwrites it
     }
