@@ -291,7 +291,8 @@ kda_status kda_gate_chunk_cumsum(const kda_fwd_desc *d, const void *g, const flo
 namespace {
 
 struct BwdLayout {
-    size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, total;
+    size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
+        off_ta, off_tb, total;
 };
 
 // After the forward's own workspace: the chunk-start states, the forward output (not
@@ -318,6 +319,14 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
     L.off_sw = L.off_sstate + f * ((size_t)p.N * p.HV * ns * p.C * p.K * 32);
     L.off_da = off;
     off = align256(off + f * Ttot * p.HV * p.K);
+    L.off_tq = off;
+    off = align256(off + f * Ttot * p.HV * p.K);
+    L.off_tk = off;
+    off = align256(off + f * Ttot * p.HV * p.K);
+    L.off_ta = off;
+    off = align256(off + f * Ttot * p.HV * p.K);
+    L.off_tb = off;
+    off = align256(off + f * Ttot * p.HV);
     L.total = off;
     return L;
 }
@@ -390,6 +399,10 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, co
     b.scr_state = reinterpret_cast<float *>(ws + L.off_sstate);
     b.scr_w = reinterpret_cast<float *>(ws + L.off_sw);
     b.scr_da = reinterpret_cast<float *>(ws + L.off_da);
+    b.t_q = reinterpret_cast<float *>(ws + L.off_tq);
+    b.t_k = reinterpret_cast<float *>(ws + L.off_tk);
+    b.t_a = reinterpret_cast<float *>(ws + L.off_ta);
+    b.t_b = reinterpret_cast<float *>(ws + L.off_tb);
     return to_status(launch_backward(b, stream));
 }
 

@@ -25,6 +25,8 @@ struct BwdParams {
     float *p_db;                    // [V / 32, Ttot, HV]
     float *scr_state, *scr_w;       // per workgroup: [C, K, 32] token states, [C, 32] w
     float *scr_da;                  // [Ttot, HV, K] dA_log terms
+    float *t_q, *t_k, *t_a;         // [Ttot, HV, K] q^, k^ (of the head's qk head), exp(g')
+    float *t_b;                     // [Ttot, HV] beta after its transform
 };
 
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C);

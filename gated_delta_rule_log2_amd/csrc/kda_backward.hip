@@ -75,63 +75,42 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x + __shfl_xor(x, 32, 64);
 }
 
-struct TokenLds {
-    float q[256], k[256], a[256];
-    float red[2][8][kSlice];
-    float wsum[4][2];
-    float b;
-};
-
-// One token's raw inputs for this thread: q, k, g of channel tid (tid < K), beta, and
-// the value-column input (v or do) of this thread's column.  Loaded a token ahead.
-struct TokenRaw {
-    float q, k, g, beta, col;
-};
-
-__device__ __forceinline__ TokenRaw load_token(const BwdParams &p, int64_t t, int h, int hv, int col,
-                                               const void *colsrc) {
-    TokenRaw r{0.f, 0.f, 0.f, 0.f, 0.f};
-    const int tid = threadIdx.x;
-    if (tid < p.K) {
-        r.q = ldf(p.q, (t * p.H + h) * p.K + tid, p.qkv_bf16);
-        r.k = ldf(p.k, (t * p.H + h) * p.K + tid, p.qkv_bf16);
-        r.g = ldf(p.g, (t * p.HV + hv) * p.K + tid, p.g_bf16);
+// Per (token, value head): q^ = scale q r_q, k^ = k r_k (r = (|x|^2 + 1e-6)^-1/2 with the
+// L2 norm, else 1), alpha = exp(g'), b, into the workspace, so the sequential kernel
+// reads them without reductions of its own.  Block of 256 threads, thread d < K.
+__global__ void __launch_bounds__(kBwdThreads) bwd_token_prep_kernel(BwdParams p) {
+    __shared__ float ws[4][2];
+    const int64_t t = blockIdx.x / p.HV;
+    const int hv = blockIdx.x % p.HV, h = hv / (p.HV / p.H), d = threadIdx.x;
+    float qv = 0.f, kv = 0.f, gp = 0.f;
+    if (d < p.K) {
+        qv = ldf(p.q, (t * p.H + h) * p.K + d, p.qkv_bf16);
+        kv = ldf(p.k, (t * p.H + h) * p.K + d, p.qkv_bf16);
+        const float ea = p.A_log ? expf(p.A_log[hv]) : 1.f;
+        const float bias = p.dt_bias ? p.dt_bias[(int64_t)hv * p.K + d] : 0.f;
+        gp = gate_nat(p, ea, bias, ldf(p.g, (t * p.HV + hv) * p.K + d, p.g_bf16));
     }
-    if (tid == 0) r.beta = ldf(p.beta, t * p.HV + hv, p.beta_bf16);
-    r.col = ldf(colsrc, (t * p.HV + hv) * p.V + col, p.qkv_bf16);
-    return r;
-}
-
-// q^, k^, alpha of a token into LDS (threads d < K), b too.  Two barriers.
-__device__ void prep_token(const BwdParams &p, TokenLds &s, const TokenRaw &x, float ea, float bias) {
-    const int tid = threadIdx.x;
-    const float qv = x.q, kv = x.k;
-    const float gp = tid < p.K ? gate_nat(p, ea, bias, x.g) : 0.f;
-    const float sq = wave_sum(qv * qv), sk = wave_sum(kv * kv);
-    if ((tid & 63) == 0) {
-        s.wsum[tid >> 6][0] = sq;
-        s.wsum[tid >> 6][1] = sk;
-    }
-    __syncthreads();
     float rq = 1.f, rk = 1.f;
     if (p.qk_l2norm) {
+        const float sq = wave_sum(qv * qv), sk = wave_sum(kv * kv);
+        if ((d & 63) == 0) ws[d >> 6][0] = sq, ws[d >> 6][1] = sk;
+        __syncthreads();
         float tq = 0.f, tk = 0.f;
-        for (int i = 0; i < kBwdThreads / 64; ++i) tq += s.wsum[i][0], tk += s.wsum[i][1];
+        for (int i = 0; i < kBwdThreads / 64; ++i) tq += ws[i][0], tk += ws[i][1];
         rq = 1.f / sqrtf(tq + 1e-6f);
         rk = 1.f / sqrtf(tk + 1e-6f);
     }
-    if (tid < p.K) {
-        s.q[tid] = qv * rq * p.scale;
-        s.k[tid] = kv * rk;
-        s.a[tid] = expf(gp);
+    const size_t o = ((size_t)t * p.HV + hv) * p.K + d;
+    if (d < p.K) {
+        p.t_q[o] = qv * rq * p.scale;
+        p.t_k[o] = kv * rk;
+        p.t_a[o] = expf(gp);
     }
-    if (tid == 0) s.b = beta_val(p, x.beta);
-    __syncthreads();
+    if (d == 0) p.t_b[t * p.HV + hv] = beta_val(p, ldf(p.beta, t * p.HV + hv, p.beta_bf16));
 }
 
 template <int NR>
 __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
-    __shared__ TokenLds s;
     const int ns = p.V / kSlice;
     const int slice = blockIdx.x % ns;
     const int hv = (blockIdx.x / ns) % p.HV;
@@ -156,136 +135,143 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     float *sc = p.scr_state + (size_t)blockIdx.x * C * K * kSlice;  // S after each token of a chunk
     float *sw = p.scr_w + (size_t)blockIdx.x * C * kSlice;          // w of each token of a chunk
 
-    const float ea = p.A_log ? expf(p.A_log[hv]) : 1.f;
-    const float bias = (p.dt_bias && tid < K) ? p.dt_bias[(int64_t)hv * K + tid] : 0.f;
-    float dS[NR], S0[NR], S[NR];
+    __shared__ float red[2][8][kSlice];
+    // one token's per-row operands (rows rg + 8 i) and this thread's column input
+    struct Rows {
+        float q[NR], k[NR], a[NR];
+        float b, col;
+    };
+    auto load_rows = [&](int64_t t, const void *colsrc, Rows &x) {
+        const size_t base = ((size_t)t * p.HV + hv) * K;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + 8 * i;
+            x.q[i] = p.t_q[base + r];
+            x.k[i] = p.t_k[base + r];
+            x.a[i] = p.t_a[base + r];
+        }
+        x.b = p.t_b[t * p.HV + hv];
+        x.col = ldf(colsrc, (t * p.HV + hv) * V + col, p.qkv_bf16);
+    };
+    float dS[NR], S0[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int r = rg + 8 * i;
-        dS[i] = (p.dht && r < K) ? p.dht[(((int64_t)n * p.HV + hv) * K + r) * V + col] : 0.f;
+        dS[i] = p.dht ? p.dht[(((int64_t)n * p.HV + hv) * K + r) * V + col] : 0.f;
     }
     int red_buf = 0;
     for (int c = nchunks - 1; c >= 0; --c) {
         const int64_t t0 = t_begin + (int64_t)c * C;
         const int64_t t1 = t0 + C < t_end ? t0 + C : t_end;
         const float *hc = p.states + ((size_t)(first_chunk + c) * p.HV + hv) * K * V;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int r = rg + 8 * i;
-            S0[i] = r < K ? hc[(size_t)r * V + col] : 0.f;
-            S[i] = S0[i];
-        }
-        // forward recompute of the chunk's token states
-        TokenRaw cur = load_token(p, t0, h, hv, col, p.v);
-        for (int64_t t = t0; t < t1; ++t) {
-            const TokenRaw nxt = t + 1 < t1 ? load_token(p, t + 1, h, hv, col, p.v) : cur;
-            prep_token(p, s, cur, ea, bias);
-            const float vj = cur.col;
-            cur = nxt;
-            float part = 0.f;
+        {
+            // forward recompute of the chunk's token states
+            float S[NR];
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
-                if (r < K) {
-                    S[i] *= s.a[r];
-                    part += S[i] * s.k[r];
-                }
+                S0[i] = hc[(size_t)(rg + 8 * i) * V + col];
+                S[i] = S0[i];
             }
-            s.red[red_buf][rg][j] = part;
-            __syncthreads();
-            float u = 0.f;
-            for (int g = 0; g < 8; ++g) u += s.red[red_buf][g][j];
-            red_buf ^= 1;
-            const float w = vj - u;
-            const int tl = (int)(t - t0);
+            Rows cur, nxt;
+            load_rows(t0, p.v, cur);
+            for (int64_t t = t0; t < t1; ++t) {
+                if (t + 1 < t1) load_rows(t + 1, p.v, nxt);
+                float part = 0.f;
 #pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
-                if (r < K) {
-                    S[i] += s.b * s.k[r] * w;
-                    sc[((size_t)tl * K + r) * kSlice + j] = S[i];
+                for (int i = 0; i < NR; ++i) {
+                    S[i] *= cur.a[i];
+                    part += S[i] * cur.k[i];
                 }
+                red[red_buf][rg][j] = part;
+                __syncthreads();
+                float u = 0.f;
+                for (int g = 0; g < 8; ++g) u += red[red_buf][g][j];
+                red_buf ^= 1;  // the next write to this buffer is two barriers away
+                const float w = cur.col - u;
+                const int tl = (int)(t - t0);
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    S[i] += cur.b * cur.k[i] * w;
+                    sc[((size_t)tl * K + rg + 8 * i) * kSlice + j] = S[i];
+                }
+                if (rg == 0) sw[tl * kSlice + j] = w;
+                if (t + 1 < t1) cur = nxt;
             }
-            if (rg == 0) sw[tl * kSlice + j] = w;
         }
         __syncthreads();  // this workgroup's scratch writes before its reads
-        // reverse token steps
-        // saved states of a token: S after it (St) and before it (Sp), and its w
-        auto load_saved = [&](int tl, float (&St)[NR], float (&Sp)[NR], float &w) {
+        // reverse token steps; St = S after token t, Sp = S before it (St of t - 1)
+        float St[NR], Sp[NR], Spn[NR];
+        auto load_before = [&](int tl, float (&dst)[NR]) {  // S before chunk token tl
 #pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
-                St[i] = sc[((size_t)tl * K + r) * kSlice + j];
-                Sp[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + r) * kSlice + j] : S0[i];
-            }
-            w = sw[tl * kSlice + j];
+            for (int i = 0; i < NR; ++i)
+                dst[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + rg + 8 * i) * kSlice + j] : S0[i];
         };
-        TokenRaw rcur = load_token(p, t1 - 1, h, hv, col, p.dout);
-        float St[NR], Sp[NR], w;
-        load_saved((int)(t1 - 1 - t0), St, Sp, w);
+        {
+            const int tl = (int)(t1 - 1 - t0);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) St[i] = sc[((size_t)tl * K + rg + 8 * i) * kSlice + j];
+            load_before(tl, Sp);
+        }
+        Rows cur, nxt;
+        load_rows(t1 - 1, p.dout, cur);
+        float w = sw[(t1 - 1 - t0) * kSlice + j];
         for (int64_t t = t1 - 1; t >= t0; --t) {
             const int tl = (int)(t - t0);
-            const TokenRaw rnxt = t > t0 ? load_token(p, t - 1, h, hv, col, p.dout) : rcur;
-            float Stn[NR], Spn[NR], wn = w;
-#pragma unroll
-            for (int i = 0; i < NR; ++i) Stn[i] = St[i], Spn[i] = Sp[i];
-            if (t > t0) load_saved(tl - 1, Stn, Spn, wn);
-            prep_token(p, s, rcur, ea, bias);
-            const float doj = rcur.col;
+            float wn = w;
+            if (t > t0) {
+                load_rows(t - 1, p.dout, nxt);
+                load_before(tl - 1, Spn);
+                wn = sw[(tl - 1) * kSlice + j];
+            }
+            const float doj = cur.col;
             const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;  // per-slice partial row
             float part = 0.f;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
-                if (r < K) {
-                    dS[i] += s.q[r] * doj;
-                    part += dS[i] * s.k[r];
-                }
+                dS[i] += cur.q[i] * doj;
+                part += dS[i] * cur.k[i];
             }
+            red[red_buf][rg][j] = part;
             // dq^ (rows of this thread), summed over the slice's columns
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
                 const float x = half_sum(St[i] * doj);
-                if (j == 0 && r < K) p.p_dq[pbase * K + r] = x;
+                if (j == 0) p.p_dq[pbase * K + rg + 8 * i] = x;
             }
-            s.red[red_buf][rg][j] = part;
             __syncthreads();
             float cj = 0.f;
-            for (int g = 0; g < 8; ++g) cj += s.red[red_buf][g][j];
+            for (int g = 0; g < 8; ++g) cj += red[red_buf][g][j];
             red_buf ^= 1;
-            const float b = s.b;
+            const float b = cur.b;
             const float e = b * cj;
             if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
             const float db = half_sum(w * cj);
             if (tid == 0) p.p_db[pbase] = db;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const int r = rg + 8 * i;
-                const float a = r < K ? s.a[r] : 0.f;
-                const float P = a * Sp[i];
+                const float P = cur.a[i] * Sp[i];
                 const float dk = half_sum(b * dS[i] * w - P * e);
-                const float dP = dS[i] - (r < K ? s.k[r] : 0.f) * e;
+                const float dP = dS[i] - cur.k[i] * e;
                 const float dgp = half_sum(dP * P);
-                if (j == 0 && r < K) {
-                    p.p_dk[pbase * K + r] = dk;
-                    p.p_dg[pbase * K + r] = dgp;
+                if (j == 0) {
+                    p.p_dk[pbase * K + rg + 8 * i] = dk;
+                    p.p_dg[pbase * K + rg + 8 * i] = dgp;
                 }
-                dS[i] = a * dP;
+                dS[i] = cur.a[i] * dP;
             }
-            rcur = rnxt;
+            if (t > t0) {
+                cur = nxt;
 #pragma unroll
-            for (int i = 0; i < NR; ++i) St[i] = Stn[i], Sp[i] = Spn[i];
-            w = wn;
+                for (int i = 0; i < NR; ++i) St[i] = Sp[i], Sp[i] = Spn[i];
+                w = wn;
+            }
         }
         __syncthreads();  // scratch reads done before the next chunk overwrites it
     }
     if (p.dh0) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int r = rg + 8 * i;
-            if (r < K) p.dh0[(((int64_t)n * p.HV + hv) * K + r) * V + col] = dS[i];
-        }
+        for (int i = 0; i < NR; ++i)
+            p.dh0[(((int64_t)n * p.HV + hv) * K + rg + 8 * i) * V + col] = dS[i];
     }
 }
 
@@ -390,6 +376,11 @@ size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C) {
 hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
     const int ns = p.V / kSlice;
     const unsigned units = (unsigned)p.N * (unsigned)p.HV * (unsigned)ns;
+    if (p.Ttot > 0) {
+        hipLaunchKernelGGL(bwd_token_prep_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (units > 0) {
         switch (p.K / 32) {
         case 1: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
