@@ -292,7 +292,7 @@ namespace {
 
 struct BwdLayout {
     size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
-        off_ta, off_tb, total;
+        off_ta, off_tb, off_param, total;
 };
 
 // After the forward's own workspace: the chunk-start states, the forward output (not
@@ -327,6 +327,8 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
     off = align256(off + f * Ttot * p.HV * p.K);
     L.off_tb = off;
     off = align256(off + f * Ttot * p.HV);
+    L.off_param = off;
+    off = align256(off + f * bwd_param_scratch_floats(p.HV, p.K));
     L.total = off;
     return L;
 }
@@ -403,6 +405,7 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, co
     b.t_k = reinterpret_cast<float *>(ws + L.off_tk);
     b.t_a = reinterpret_cast<float *>(ws + L.off_ta);
     b.t_b = reinterpret_cast<float *>(ws + L.off_tb);
+    b.scr_param = reinterpret_cast<float *>(ws + L.off_param);
     return to_status(launch_backward(b, stream));
 }
 

@@ -27,9 +27,11 @@ struct BwdParams {
     float *scr_da;                  // [Ttot, HV, K] dA_log terms
     float *t_q, *t_k, *t_a;         // [Ttot, HV, K] q^, k^ (of the head's qk head), exp(g')
     float *t_b;                     // [Ttot, HV] beta after its transform
+    float *scr_param;               // [HV, 64, K + 1] per-segment dt_bias / A_log sums
 };
 
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C);
+size_t bwd_param_scratch_floats(int HV, int K);
 hipError_t launch_backward(const BwdParams &p, hipStream_t s);
 
 }  // namespace kda

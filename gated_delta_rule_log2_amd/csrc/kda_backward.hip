@@ -348,26 +348,49 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_gate_kernel(BwdParams p) {
     }
 }
 
-// dt_bias and A_log gradients: sums over tokens (and channels for A_log), one block
-// per value head, tokens in order.
-__global__ void __launch_bounds__(kBwdThreads) bwd_param_kernel(BwdParams p) {
+// dt_bias and A_log gradients: sums over tokens (and channels for A_log).  First per
+// (value head, token segment), then the segments in order, so the result does not
+// depend on scheduling.
+constexpr int kParamSegs = 64;
+
+__global__ void __launch_bounds__(kBwdThreads) bwd_param_partial_kernel(BwdParams p) {
     __shared__ float ws[4];
-    const int hv = blockIdx.x, d = threadIdx.x;
+    const int hv = blockIdx.x / kParamSegs, seg = blockIdx.x % kParamSegs, d = threadIdx.x;
+    const int64_t per = (p.Ttot + kParamSegs - 1) / kParamSegs;
+    const int64_t ta = seg * per, tb = ta + per < p.Ttot ? ta + per : p.Ttot;
     float sdg = 0.f, sda = 0.f;
     if (d < p.K)
-        for (int64_t t = 0; t < p.Ttot; ++t) {
+        for (int64_t t = ta; t < tb; ++t) {
             const size_t idx = (t * p.HV + hv) * p.K + d;
             sdg += p.dg[idx];
             sda += p.scr_da[idx];
         }
-    if (p.ddt_bias && d < p.K) p.ddt_bias[(int64_t)hv * p.K + d] = sdg;
+    float *part = p.scr_param + (size_t)(hv * kParamSegs + seg) * (p.K + 1);
+    if (d < p.K) part[d] = sdg;
     const float r = wave_sum(sda);
     if ((d & 63) == 0) ws[d >> 6] = r;
     __syncthreads();
-    if (d == 0 && p.dA_log) p.dA_log[hv] = ws[0] + ws[1] + ws[2] + ws[3];
+    if (d == 0) part[p.K] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+__global__ void __launch_bounds__(kBwdThreads) bwd_param_kernel(BwdParams p) {
+    const int hv = blockIdx.x, d = threadIdx.x;
+    const float *part = p.scr_param + (size_t)hv * kParamSegs * (p.K + 1);
+    if (d < p.K && p.ddt_bias) {
+        float acc = 0.f;
+        for (int seg = 0; seg < kParamSegs; ++seg) acc += part[(size_t)seg * (p.K + 1) + d];
+        p.ddt_bias[(int64_t)hv * p.K + d] = acc;
+    }
+    if (d == 0 && p.dA_log) {
+        float acc = 0.f;
+        for (int seg = 0; seg < kParamSegs; ++seg) acc += part[(size_t)seg * (p.K + 1) + p.K];
+        p.dA_log[hv] = acc;
+    }
 }
 
 }  // namespace
+
+size_t bwd_param_scratch_floats(int HV, int K) { return (size_t)HV * kParamSegs * (K + 1); }
 
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C) {
     return (size_t)N * HV * (V / kSlice) * C * ((size_t)K * kSlice + kSlice);
@@ -400,7 +423,10 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
         hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)(p.Ttot * p.H)), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);
     }
-    if (p.gate_mode != kGatePre) hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, p);
+    if (p.gate_mode != kGatePre) {
+        hipLaunchKernelGGL(bwd_param_partial_kernel, dim3((unsigned)p.HV * kParamSegs), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 
