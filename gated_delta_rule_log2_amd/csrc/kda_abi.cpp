@@ -299,7 +299,7 @@ struct BwdLayout {
 // returned), the per-slice partial sums and the per-workgroup token-state scratch.
 BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
     BwdLayout L{};
-    const size_t Ttot = (size_t)p.B * p.T, ns = (size_t)p.V / 32, f = sizeof(float);
+    const size_t Ttot = (size_t)p.B * p.T, ns = (size_t)bwd_slices(p.V), f = sizeof(float);
     size_t off = align256(fwd_bytes);
     L.off_states = off;
     off = align256(off + f * (size_t)p.total_chunks * p.HV * p.K * p.V);
@@ -316,7 +316,7 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
     const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
     L.off_sstate = off;
     off = align256(off + f * scr);
-    L.off_sw = L.off_sstate + f * ((size_t)p.N * p.HV * ns * p.C * p.K * 32);
+    L.off_sw = L.off_sstate + f * bwd_seq_state_floats(p.N, p.HV, p.K, p.V, p.C);
     L.off_da = off;
     off = align256(off + f * Ttot * p.HV * p.K);
     L.off_tq = off;

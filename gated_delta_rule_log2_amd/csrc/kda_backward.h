@@ -21,15 +21,17 @@ struct BwdParams {
     // outputs (fp32); dA_log, ddt_bias, dh0 may be nullptr
     float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt_bias, *dh0;
     // workspace
-    float *p_dq, *p_dk, *p_dg;      // [V / 32, Ttot, HV, K] per-slice sums over V
-    float *p_db;                    // [V / 32, Ttot, HV]
-    float *scr_state, *scr_w;       // per workgroup: [C, K, 32] token states, [C, 32] w
+    float *p_dq, *p_dk, *p_dg;      // [slices, Ttot, HV, K] per-slice sums over V
+    float *p_db;                    // [slices, Ttot, HV]
+    float *scr_state, *scr_w;       // per workgroup: [C, K, slice] token states, [C, slice] w
     float *scr_da;                  // [Ttot, HV, K] dA_log terms
     float *t_q, *t_k, *t_a;         // [Ttot, HV, K] q^, k^ (of the head's qk head), exp(g')
     float *t_b;                     // [Ttot, HV] beta after its transform
     float *scr_param;               // [HV, 64, K + 1] per-segment dt_bias / A_log sums
 };
 
+int bwd_slices(int V);
+size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C);
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C);
 size_t bwd_param_scratch_floats(int HV, int K);
 hipError_t launch_backward(const BwdParams &p, hipStream_t s);

@@ -4,7 +4,7 @@
 //
 // A first, token-level form.  The forward runs first and keeps the state each chunk
 // starts from (the same kernels as the forward entry, with intermediate states).  Then
-// one workgroup per (sequence, value head, 32-column slice of V) walks its chunks last
+// one workgroup per (sequence, value head, 16-column slice of V) walks its chunks last
 // to first: it recomputes the chunk's token states from the chunk-start state, then
 // takes the reverse token step (per token, with P = Diag(alpha) S_prev, u = P^T k^,
 // w = v - u, S = P + b k^ w^T):
@@ -22,8 +22,9 @@ namespace kda {
 
 namespace {
 
-constexpr int kBwdThreads = 256;  // 8 row groups x 32 columns
-constexpr int kSlice = 32;
+constexpr int kBwdThreads = 256;  // kRowGroups row groups x kSlice columns
+constexpr int kSlice = 16;
+constexpr int kRowGroups = kBwdThreads / kSlice;
 
 __device__ __forceinline__ float ldf(const void *p, int64_t i, bool bf) {
     if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
@@ -116,10 +117,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     const int hv = (blockIdx.x / ns) % p.HV;
     const int n = blockIdx.x / (ns * p.HV);
     const int h = hv / (p.HV / p.H);
-    const int tid = threadIdx.x, j = tid & (kSlice - 1), rg = tid >> 5;
+    const int tid = threadIdx.x, j = tid & (kSlice - 1), rg = tid / kSlice;
     const int col = slice * kSlice + j;
     const int K = p.K, V = p.V, C = p.C;
-    // rows of this thread: rg + 8 i
+    // rows of this thread: rg + kRowGroups i
     int64_t t_begin, t_end, first_chunk = 0;
     if (p.cu_seqlens) {
         t_begin = p.cu_seqlens[n];
@@ -135,8 +136,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     float *sc = p.scr_state + (size_t)blockIdx.x * C * K * kSlice;  // S after each token of a chunk
     float *sw = p.scr_w + (size_t)blockIdx.x * C * kSlice;          // w of each token of a chunk
 
-    __shared__ float red[2][8][kSlice];
-    // one token's per-row operands (rows rg + 8 i) and this thread's column input
+    __shared__ float red[2][kRowGroups][kSlice];
+    // one token's per-row operands (rows rg + kRowGroups i) and this thread's column input
     struct Rows {
         float q[NR], k[NR], a[NR];
         float b, col;
@@ -145,7 +146,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
         const size_t base = ((size_t)t * p.HV + hv) * K;
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int r = rg + 8 * i;
+            const int r = rg + kRowGroups * i;
             x.q[i] = p.t_q[base + r];
             x.k[i] = p.t_k[base + r];
             x.a[i] = p.t_a[base + r];
@@ -156,7 +157,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     float dS[NR], S0[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int r = rg + 8 * i;
+        const int r = rg + kRowGroups * i;
         dS[i] = p.dht ? p.dht[(((int64_t)n * p.HV + hv) * K + r) * V + col] : 0.f;
     }
     int red_buf = 0;
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
             float S[NR];
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                S0[i] = hc[(size_t)(rg + 8 * i) * V + col];
+                S0[i] = hc[(size_t)(rg + kRowGroups * i) * V + col];
                 S[i] = S0[i];
             }
             Rows cur, nxt;
@@ -185,14 +186,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
                 red[red_buf][rg][j] = part;
                 __syncthreads();
                 float u = 0.f;
-                for (int g = 0; g < 8; ++g) u += red[red_buf][g][j];
+                for (int g = 0; g < kRowGroups; ++g) u += red[red_buf][g][j];
                 red_buf ^= 1;  // the next write to this buffer is two barriers away
                 const float w = cur.col - u;
                 const int tl = (int)(t - t0);
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
                     S[i] += cur.b * cur.k[i] * w;
-                    sc[((size_t)tl * K + rg + 8 * i) * kSlice + j] = S[i];
+                    sc[((size_t)tl * K + rg + kRowGroups * i) * kSlice + j] = S[i];
                 }
                 if (rg == 0) sw[tl * kSlice + j] = w;
                 if (t + 1 < t1) cur = nxt;
@@ -204,12 +205,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
         auto load_before = [&](int tl, float (&dst)[NR]) {  // S before chunk token tl
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                dst[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + rg + 8 * i) * kSlice + j] : S0[i];
+                dst[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + rg + kRowGroups * i) * kSlice + j] : S0[i];
         };
         {
             const int tl = (int)(t1 - 1 - t0);
 #pragma unroll
-            for (int i = 0; i < NR; ++i) St[i] = sc[((size_t)tl * K + rg + 8 * i) * kSlice + j];
+            for (int i = 0; i < NR; ++i) St[i] = sc[((size_t)tl * K + rg + kRowGroups * i) * kSlice + j];
             load_before(tl, Sp);
         }
         Rows cur, nxt;
@@ -235,27 +236,27 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
             // dq^ (rows of this thread), summed over the slice's columns
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const float x = half_sum(St[i] * doj);
-                if (j == 0) p.p_dq[pbase * K + rg + 8 * i] = x;
+                const float x = row_sum16(St[i] * doj);
+                if (j == 0) p.p_dq[pbase * K + rg + kRowGroups * i] = x;
             }
             __syncthreads();
             float cj = 0.f;
-            for (int g = 0; g < 8; ++g) cj += red[red_buf][g][j];
+            for (int g = 0; g < kRowGroups; ++g) cj += red[red_buf][g][j];
             red_buf ^= 1;
             const float b = cur.b;
             const float e = b * cj;
             if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
-            const float db = half_sum(w * cj);
+            const float db = row_sum16(w * cj);
             if (tid == 0) p.p_db[pbase] = db;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const float P = cur.a[i] * Sp[i];
-                const float dk = half_sum(b * dS[i] * w - P * e);
+                const float dk = row_sum16(b * dS[i] * w - P * e);
                 const float dP = dS[i] - cur.k[i] * e;
-                const float dgp = half_sum(dP * P);
+                const float dgp = row_sum16(dP * P);
                 if (j == 0) {
-                    p.p_dk[pbase * K + rg + 8 * i] = dk;
-                    p.p_dg[pbase * K + rg + 8 * i] = dgp;
+                    p.p_dk[pbase * K + rg + kRowGroups * i] = dk;
+                    p.p_dg[pbase * K + rg + kRowGroups * i] = dgp;
                 }
                 dS[i] = cur.a[i] * dP;
             }
@@ -271,7 +272,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
     if (p.dh0) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
-            p.dh0[(((int64_t)n * p.HV + hv) * K + rg + 8 * i) * V + col] = dS[i];
+            p.dh0[(((int64_t)n * p.HV + hv) * K + rg + kRowGroups * i) * V + col] = dS[i];
     }
 }
 
@@ -392,8 +393,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_param_kernel(BwdParams p) {
 
 size_t bwd_param_scratch_floats(int HV, int K) { return (size_t)HV * kParamSegs * (K + 1); }
 
+int bwd_slices(int V) { return V / kSlice; }
+
+size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C) {
+    return (size_t)N * HV * (V / kSlice) * C * (size_t)K * kSlice;
+}
+
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C) {
-    return (size_t)N * HV * (V / kSlice) * C * ((size_t)K * kSlice + kSlice);
+    return bwd_seq_state_floats(N, HV, K, V, C) + (size_t)N * HV * (V / kSlice) * C * kSlice;
 }
 
 hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
@@ -406,14 +413,14 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
     }
     if (units > 0) {
         switch (p.K / 32) {
-        case 1: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 2: hipLaunchKernelGGL(bwd_seq_kernel<8>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 3: hipLaunchKernelGGL(bwd_seq_kernel<12>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 4: hipLaunchKernelGGL(bwd_seq_kernel<16>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 5: hipLaunchKernelGGL(bwd_seq_kernel<20>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 6: hipLaunchKernelGGL(bwd_seq_kernel<24>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 7: hipLaunchKernelGGL(bwd_seq_kernel<28>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 8: hipLaunchKernelGGL(bwd_seq_kernel<32>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 1: hipLaunchKernelGGL(bwd_seq_kernel<2>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 3: hipLaunchKernelGGL(bwd_seq_kernel<6>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 4: hipLaunchKernelGGL(bwd_seq_kernel<8>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 5: hipLaunchKernelGGL(bwd_seq_kernel<10>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 6: hipLaunchKernelGGL(bwd_seq_kernel<12>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 7: hipLaunchKernelGGL(bwd_seq_kernel<14>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 8: hipLaunchKernelGGL(bwd_seq_kernel<16>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
         default: return hipErrorInvalidValue;
         }
         hipError_t e = hipGetLastError();
