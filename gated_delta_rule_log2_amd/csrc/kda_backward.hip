@@ -22,9 +22,10 @@ namespace kda {
 
 namespace {
 
-constexpr int kBwdThreads = 256;  // kRowGroups row groups x kSlice columns
+constexpr int kBwdThreads = 256;  // the per-token and per-head kernels
+constexpr int kSeqThreads = 512;  // the sequential kernel: kRowGroups row groups x kSlice columns
 constexpr int kSlice = 16;
-constexpr int kRowGroups = kBwdThreads / kSlice;
+constexpr int kRowGroups = kSeqThreads / kSlice;
 
 __device__ __forceinline__ float ldf(const void *p, int64_t i, bool bf) {
     if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
@@ -111,7 +112,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_token_prep_kernel(BwdParams p
 }
 
 template <int NR>
-__global__ void __launch_bounds__(kBwdThreads) bwd_seq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     const int ns = p.V / kSlice;
     const int slice = blockIdx.x % ns;
     const int hv = (blockIdx.x / ns) % p.HV;
@@ -413,14 +414,14 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
     }
     if (units > 0) {
         switch (p.K / 32) {
-        case 1: hipLaunchKernelGGL(bwd_seq_kernel<2>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 2: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 3: hipLaunchKernelGGL(bwd_seq_kernel<6>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 4: hipLaunchKernelGGL(bwd_seq_kernel<8>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 5: hipLaunchKernelGGL(bwd_seq_kernel<10>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 6: hipLaunchKernelGGL(bwd_seq_kernel<12>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 7: hipLaunchKernelGGL(bwd_seq_kernel<14>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
-        case 8: hipLaunchKernelGGL(bwd_seq_kernel<16>, dim3(units), dim3(kBwdThreads), 0, s, p); break;
+        case 1: hipLaunchKernelGGL(bwd_seq_kernel<1>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(bwd_seq_kernel<2>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 3: hipLaunchKernelGGL(bwd_seq_kernel<3>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 4: hipLaunchKernelGGL(bwd_seq_kernel<4>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 5: hipLaunchKernelGGL(bwd_seq_kernel<5>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 6: hipLaunchKernelGGL(bwd_seq_kernel<6>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 7: hipLaunchKernelGGL(bwd_seq_kernel<7>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
+        case 8: hipLaunchKernelGGL(bwd_seq_kernel<8>, dim3(units), dim3(kSeqThreads), 0, s, p); break;
         default: return hipErrorInvalidValue;
         }
         hipError_t e = hipGetLastError();
