@@ -189,3 +189,33 @@ def test_transposed_state_flag_and_states_entry_checks(lib):
     rc = lib.kda_chunk_fwd_states(ctypes.byref(d), *([None] * 13), 0, None)
     assert _abi.STATUS_NAMES[rc] == "KDA_ERR_NULL_POINTER"
 
+
+
+def bwd_status(lib, d, **ptrs):
+    names = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "h0", "cu", "do", "dht", "dq", "dk", "dv", "dg",
+             "dbeta", "dA_log", "ddt_bias", "dh0", "ws"]
+    ws_bytes = ptrs.pop("ws_bytes", 1 << 40)
+    p = {n: FAKE for n in names}
+    p.update(dt_bias=None, h0=None, cu=None, dht=None, dA_log=None, ddt_bias=None, dh0=None)
+    p.update(ptrs)
+    return lib.kda_chunk_bwd(ctypes.byref(d), *[p[n] for n in names], ws_bytes, None)
+
+
+def test_backward_entry_checks(lib):
+    """kda_chunk_bwd: the forward's descriptor checks, the transposed state layout refused,
+    missing inputs / outputs / workspace refused before anything is enqueued."""
+    n = ctypes.c_size_t(0)
+    assert _abi.STATUS_NAMES[lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n))] == "KDA_OK"
+    fwd_need = ws_status(lib, desc())[1]
+    assert n.value > fwd_need  # the forward's workspace plus the backward's own
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc()), None) == S["KDA_ERR_NULL_POINTER"]
+    rc = lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc(flags=_abi.TRANSPOSE_STATE)), ctypes.byref(n))
+    assert _abi.STATUS_NAMES[rc] == "KDA_ERR_UNSUPPORTED"
+    assert bwd_status(lib, desc(chunk_size=48)) == S["KDA_ERR_CHUNK_SIZE"]
+    assert bwd_status(lib, desc(H=3, HV=4)) == S["KDA_ERR_GVA"]
+    for missing in ("do", "dq", "dk", "dv", "dg", "dbeta", "q"):
+        assert bwd_status(lib, desc(), **{missing: None}) == S["KDA_ERR_NULL_POINTER"], missing
+    assert bwd_status(lib, desc(flags=_abi.GATE_IN_KERNEL), A_log=None) == S["KDA_ERR_MISSING_A_LOG"]
+    assert bwd_status(lib, desc(), ws=None) == S["KDA_ERR_WORKSPACE"]
+    lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n))
+    assert bwd_status(lib, desc(), ws_bytes=n.value - 1) == S["KDA_ERR_WORKSPACE"]
