@@ -98,9 +98,13 @@ class Hip:
 
 
 def source_digest() -> str:
+    """Digest of the forward path's sources: every file under csrc/ except the backward's
+    own kernels (kda_backward.*), which the forward's kernels neither include nor launch."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_log2_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name.startswith("kda_backward."):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
