@@ -23,9 +23,10 @@ namespace kda {
 namespace {
 
 constexpr int kBwdThreads = 256;  // the per-token and per-head kernels
-constexpr int kSeqThreads = 512;  // the sequential kernel: kRowGroups row groups x kSlice columns
+constexpr int kRoleThreads = 512;  // per role of the sequential kernel: kRowGroups row groups x kSlice columns
+constexpr int kSeqThreads = 2 * kRoleThreads;
 constexpr int kSlice = 16;
-constexpr int kRowGroups = kSeqThreads / kSlice;
+constexpr int kRowGroups = kRoleThreads / kSlice;
 
 __device__ __forceinline__ float ldf(const void *p, int64_t i, bool bf) {
     if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
@@ -111,14 +112,21 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_token_prep_kernel(BwdParams p
     if (d == 0) p.t_b[t * p.HV + hv] = beta_val(p, ldf(p.beta, t * p.HV + hv, p.beta_bf16));
 }
 
+// Two roles of 512 threads each, run side by side: role 1 recomputes the token states
+// of chunk c - 1 (from its chunk-start state, into scratch buffer (c - 1) & 1) while
+// role 0 takes the reverse steps of chunk c (from buffer c & 1).  Phase ph handles
+// recompute chunk ph - 1 and reverse chunk ph; both roles run max(lengths) steps with
+// one workgroup barrier per step, outside any role-dependent branch, and one barrier
+// between phases, so the barrier counts of the two roles always match.
 template <int NR>
 __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     const int ns = p.V / kSlice;
     const int slice = blockIdx.x % ns;
     const int hv = (blockIdx.x / ns) % p.HV;
     const int n = blockIdx.x / (ns * p.HV);
-    const int h = hv / (p.HV / p.H);
-    const int tid = threadIdx.x, j = tid & (kSlice - 1), rg = tid / kSlice;
+    const int tid = threadIdx.x;
+    const int role = tid / kRoleThreads;  // 0: reverse steps, 1: recompute (wave-uniform)
+    const int lt = tid % kRoleThreads, j = lt & (kSlice - 1), rg = lt / kSlice;
     const int col = slice * kSlice + j;
     const int K = p.K, V = p.V, C = p.C;
     // rows of this thread: rg + kRowGroups i
@@ -134,10 +142,16 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     }
     const int64_t len = t_end - t_begin;
     const int nchunks = (int)((len + C - 1) / C);
-    float *sc = p.scr_state + (size_t)blockIdx.x * C * K * kSlice;  // S after each token of a chunk
-    float *sw = p.scr_w + (size_t)blockIdx.x * C * kSlice;          // w of each token of a chunk
+    auto chunk_len = [&](int c) -> int {
+        if (c < 0 || c >= nchunks) return 0;
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        return (int)((t0 + C < t_end ? t0 + C : t_end) - t0);
+    };
+    // two scratch buffers: S after each token of a chunk, and each token's w
+    auto sc = [&](int buf) { return p.scr_state + ((size_t)blockIdx.x * 2 + buf) * C * K * kSlice; };
+    auto sw = [&](int buf) { return p.scr_w + ((size_t)blockIdx.x * 2 + buf) * C * kSlice; };
 
-    __shared__ float red[2][kRowGroups][kSlice];
+    __shared__ float red[2][2][kRowGroups][kSlice];  // [role][parity][row group][column]
     // one token's per-row operands (rows rg + kRowGroups i) and this thread's column input
     struct Rows {
         float q[NR], k[NR], a[NR];
@@ -155,122 +169,131 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
         x.b = p.t_b[t * p.HV + hv];
         x.col = ldf(colsrc, (t * p.HV + hv) * V + col, p.qkv_bf16);
     };
-    float dS[NR], S0[NR];
+    auto load_start = [&](int c, float (&dst)[NR]) {  // state chunk c starts from
+        const float *hc = p.states + ((size_t)(first_chunk + c) * p.HV + hv) * K * V;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) dst[i] = hc[(size_t)(rg + kRowGroups * i) * V + col];
+    };
+
+    // role 0 (reverse) state
+    float dS[NR], S0[NR], St[NR], Sp[NR], Spn[NR], w = 0.f, wn = 0.f, part = 0.f, doj = 0.f;
+    // role 1 (recompute) state
+    float S[NR];
+    Rows cur, nxt;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int r = rg + kRowGroups * i;
-        dS[i] = p.dht ? p.dht[(((int64_t)n * p.HV + hv) * K + r) * V + col] : 0.f;
+        dS[i] = (role == 0 && p.dht) ? p.dht[(((int64_t)n * p.HV + hv) * K + rg + kRowGroups * i) * V + col] : 0.f;
+        S0[i] = St[i] = Sp[i] = Spn[i] = S[i] = 0.f;
     }
-    int red_buf = 0;
-    for (int c = nchunks - 1; c >= 0; --c) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int64_t t1 = t0 + C < t_end ? t0 + C : t_end;
-        const float *hc = p.states + ((size_t)(first_chunk + c) * p.HV + hv) * K * V;
-        {
-            // forward recompute of the chunk's token states
-            float S[NR];
+    int parity = 0;
+    for (int ph = nchunks; ph >= 0; --ph) {
+        const int cr = ph - 1, cv = ph;  // chunk recomputed, chunk reversed
+        const int lr = chunk_len(cr), lv = chunk_len(cv);
+        const int nst = lr > lv ? lr : lv;
+        const int64_t t0r = t_begin + (int64_t)cr * C, t0v = t_begin + (int64_t)cv * C;
+        float *scr = sc(cr & 1), *swr = sw(cr & 1);
+        const float *scv = sc(cv & 1), *swv = sw(cv & 1);
+        if (role == 1 && lr > 0) {
+            load_start(cr, S);
+            load_rows(t0r, p.v, cur);
+        }
+        if (role == 0 && lv > 0) {
+            load_start(cv, S0);
+            const int tl = lv - 1;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                S0[i] = hc[(size_t)(rg + kRowGroups * i) * V + col];
-                S[i] = S0[i];
+                St[i] = scv[((size_t)tl * K + rg + kRowGroups * i) * kSlice + j];
+                Sp[i] = tl > 0 ? scv[((size_t)(tl - 1) * K + rg + kRowGroups * i) * kSlice + j] : S0[i];
             }
-            Rows cur, nxt;
-            load_rows(t0, p.v, cur);
-            for (int64_t t = t0; t < t1; ++t) {
-                if (t + 1 < t1) load_rows(t + 1, p.v, nxt);
-                float part = 0.f;
+            w = swv[tl * kSlice + j];
+            load_rows(t0v + tl, p.dout, cur);
+        }
+        for (int st = 0; st < nst; ++st) {
+            // ---- before the step's barrier
+            if (role == 1 && st < lr) {
+                if (st + 1 < lr) load_rows(t0r + st + 1, p.v, nxt);
+                part = 0.f;
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
                     S[i] *= cur.a[i];
                     part += S[i] * cur.k[i];
                 }
-                red[red_buf][rg][j] = part;
-                __syncthreads();
-                float u = 0.f;
-                for (int g = 0; g < kRowGroups; ++g) u += red[red_buf][g][j];
-                red_buf ^= 1;  // the next write to this buffer is two barriers away
-                const float w = cur.col - u;
-                const int tl = (int)(t - t0);
+                red[1][parity][rg][j] = part;
+            }
+            if (role == 0 && st < lv) {
+                const int tl = lv - 1 - st;
+                const int64_t t = t0v + tl;
+                if (tl > 0) {
+                    load_rows(t - 1, p.dout, nxt);
+#pragma unroll
+                    for (int i = 0; i < NR; ++i)
+                        Spn[i] = tl - 1 > 0 ? scv[((size_t)(tl - 2) * K + rg + kRowGroups * i) * kSlice + j] : S0[i];
+                    wn = swv[(tl - 1) * kSlice + j];
+                }
+                doj = cur.col;
+                const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;
+                part = 0.f;
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    S[i] += cur.b * cur.k[i] * w;
-                    sc[((size_t)tl * K + rg + kRowGroups * i) * kSlice + j] = S[i];
+                    dS[i] += cur.q[i] * doj;
+                    part += dS[i] * cur.k[i];
                 }
-                if (rg == 0) sw[tl * kSlice + j] = w;
-                if (t + 1 < t1) cur = nxt;
-            }
-        }
-        __syncthreads();  // this workgroup's scratch writes before its reads
-        // reverse token steps; St = S after token t, Sp = S before it (St of t - 1)
-        float St[NR], Sp[NR], Spn[NR];
-        auto load_before = [&](int tl, float (&dst)[NR]) {  // S before chunk token tl
+                red[0][parity][rg][j] = part;
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                dst[i] = tl > 0 ? sc[((size_t)(tl - 1) * K + rg + kRowGroups * i) * kSlice + j] : S0[i];
-        };
-        {
-            const int tl = (int)(t1 - 1 - t0);
-#pragma unroll
-            for (int i = 0; i < NR; ++i) St[i] = sc[((size_t)tl * K + rg + kRowGroups * i) * kSlice + j];
-            load_before(tl, Sp);
-        }
-        Rows cur, nxt;
-        load_rows(t1 - 1, p.dout, cur);
-        float w = sw[(t1 - 1 - t0) * kSlice + j];
-        for (int64_t t = t1 - 1; t >= t0; --t) {
-            const int tl = (int)(t - t0);
-            float wn = w;
-            if (t > t0) {
-                load_rows(t - 1, p.dout, nxt);
-                load_before(tl - 1, Spn);
-                wn = sw[(tl - 1) * kSlice + j];
-            }
-            const float doj = cur.col;
-            const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;  // per-slice partial row
-            float part = 0.f;
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                dS[i] += cur.q[i] * doj;
-                part += dS[i] * cur.k[i];
-            }
-            red[red_buf][rg][j] = part;
-            // dq^ (rows of this thread), summed over the slice's columns
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const float x = row_sum16(St[i] * doj);
-                if (j == 0) p.p_dq[pbase * K + rg + kRowGroups * i] = x;
+                for (int i = 0; i < NR; ++i) {  // dq^ rows, summed over the slice's columns
+                    const float x = row_sum16(St[i] * doj);
+                    if (j == 0) p.p_dq[pbase * K + rg + kRowGroups * i] = x;
+                }
             }
             __syncthreads();
-            float cj = 0.f;
-            for (int g = 0; g < kRowGroups; ++g) cj += red[red_buf][g][j];
-            red_buf ^= 1;
-            const float b = cur.b;
-            const float e = b * cj;
-            if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
-            const float db = row_sum16(w * cj);
-            if (tid == 0) p.p_db[pbase] = db;
+            // ---- after it
+            if (role == 1 && st < lr) {
+                float u = 0.f;
+                for (int g = 0; g < kRowGroups; ++g) u += red[1][parity][g][j];
+                const float wv = cur.col - u;
 #pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const float P = cur.a[i] * Sp[i];
-                const float dk = row_sum16(b * dS[i] * w - P * e);
-                const float dP = dS[i] - cur.k[i] * e;
-                const float dgp = row_sum16(dP * P);
-                if (j == 0) {
-                    p.p_dk[pbase * K + rg + kRowGroups * i] = dk;
-                    p.p_dg[pbase * K + rg + kRowGroups * i] = dgp;
+                for (int i = 0; i < NR; ++i) {
+                    S[i] += cur.b * cur.k[i] * wv;
+                    scr[((size_t)st * K + rg + kRowGroups * i) * kSlice + j] = S[i];
                 }
-                dS[i] = cur.a[i] * dP;
+                if (rg == 0) swr[st * kSlice + j] = wv;
+                if (st + 1 < lr) cur = nxt;
             }
-            if (t > t0) {
-                cur = nxt;
+            if (role == 0 && st < lv) {
+                const int tl = lv - 1 - st;
+                const int64_t t = t0v + tl;
+                const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;
+                float cj = 0.f;
+                for (int g = 0; g < kRowGroups; ++g) cj += red[0][parity][g][j];
+                const float b = cur.b;
+                const float e = b * cj;
+                if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
+                const float db = row_sum16(w * cj);
+                if (lt == 0) p.p_db[pbase] = db;
 #pragma unroll
-                for (int i = 0; i < NR; ++i) St[i] = Sp[i], Sp[i] = Spn[i];
-                w = wn;
+                for (int i = 0; i < NR; ++i) {
+                    const float P = cur.a[i] * Sp[i];
+                    const float dk = row_sum16(b * dS[i] * w - P * e);
+                    const float dP = dS[i] - cur.k[i] * e;
+                    const float dgp = row_sum16(dP * P);
+                    if (j == 0) {
+                        p.p_dk[pbase * K + rg + kRowGroups * i] = dk;
+                        p.p_dg[pbase * K + rg + kRowGroups * i] = dgp;
+                    }
+                    dS[i] = cur.a[i] * dP;
+                }
+                if (tl > 0) {
+                    cur = nxt;
+#pragma unroll
+                    for (int i = 0; i < NR; ++i) St[i] = Sp[i], Sp[i] = Spn[i];
+                    w = wn;
+                }
             }
+            parity ^= 1;  // the next write to this parity's buffers is a barrier away from its reads
         }
-        __syncthreads();  // scratch reads done before the next chunk overwrites it
+        __syncthreads();  // scratch written in this phase is read in the next; read buffers are refilled after it
     }
-    if (p.dh0) {
+    if (role == 0 && p.dh0) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
             p.dh0[(((int64_t)n * p.HV + hv) * K + rg + kRowGroups * i) * V + col] = dS[i];
@@ -396,12 +419,12 @@ size_t bwd_param_scratch_floats(int HV, int K) { return (size_t)HV * kParamSegs 
 
 int bwd_slices(int V) { return V / kSlice; }
 
-size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C) {
-    return (size_t)N * HV * (V / kSlice) * C * (size_t)K * kSlice;
+size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C) {  // two buffers per workgroup
+    return (size_t)N * HV * (V / kSlice) * 2 * C * (size_t)K * kSlice;
 }
 
 size_t bwd_seq_scratch_floats(int N, int HV, int K, int V, int C) {
-    return bwd_seq_state_floats(N, HV, K, V, C) + (size_t)N * HV * (V / kSlice) * C * kSlice;
+    return bwd_seq_state_floats(N, HV, K, V, C) + (size_t)N * HV * (V / kSlice) * 2 * C * kSlice;
 }
 
 hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
