@@ -151,7 +151,8 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     auto sc = [&](int buf) { return p.scr_state + ((size_t)blockIdx.x * 2 + buf) * C * K * kSlice; };
     auto sw = [&](int buf) { return p.scr_w + ((size_t)blockIdx.x * 2 + buf) * C * kSlice; };
 
-    __shared__ float red[2][2][kRowGroups][kSlice];  // [role][parity][row group][column]
+    // per-wave column sums: [role][parity][wave of the role][column]
+    __shared__ float red[2][2][kRoleThreads / 64][kSlice];
     // one token's per-row operands (rows rg + kRowGroups i) and this thread's column input
     struct Rows {
         float q[NR], k[NR], a[NR];
@@ -218,7 +219,9 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
                     S[i] *= cur.a[i];
                     part += S[i] * cur.k[i];
                 }
-                red[1][parity][rg][j] = part;
+                part += __shfl_xor(part, 16, 64);  // the wave's four row groups
+                part += __shfl_xor(part, 32, 64);
+                if ((lt & 63) < kSlice) red[1][parity][lt >> 6][j] = part;
             }
             if (role == 0 && st < lv) {
                 const int tl = lv - 1 - st;
@@ -238,7 +241,9 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
                     dS[i] += cur.q[i] * doj;
                     part += dS[i] * cur.k[i];
                 }
-                red[0][parity][rg][j] = part;
+                part += __shfl_xor(part, 16, 64);
+                part += __shfl_xor(part, 32, 64);
+                if ((lt & 63) < kSlice) red[0][parity][lt >> 6][j] = part;
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {  // dq^ rows, summed over the slice's columns
                     const float x = row_sum16(St[i] * doj);
@@ -249,7 +254,7 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
             // ---- after it
             if (role == 1 && st < lr) {
                 float u = 0.f;
-                for (int g = 0; g < kRowGroups; ++g) u += red[1][parity][g][j];
+                for (int g = 0; g < kRoleThreads / 64; ++g) u += red[1][parity][g][j];
                 const float wv = cur.col - u;
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
@@ -264,7 +269,7 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
                 const int64_t t = t0v + tl;
                 const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;
                 float cj = 0.f;
-                for (int g = 0; g < kRowGroups; ++g) cj += red[0][parity][g][j];
+                for (int g = 0; g < kRoleThreads / 64; ++g) cj += red[0][parity][g][j];
                 const float b = cur.b;
                 const float e = b * cj;
                 if (rg == 0) p.dv[(t * p.HV + hv) * V + col] = e;
