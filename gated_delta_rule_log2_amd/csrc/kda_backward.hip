@@ -156,8 +156,10 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     // one token's per-row operands (rows rg + kRowGroups i) and this thread's column input
     struct Rows {
         float q[NR], k[NR], a[NR];
-        float b, col;
+        float b;
+        uint32_t col;  // raw bits of the column input (widened at its use, so the load can stay in flight)
     };
+    auto colval = [&](uint32_t raw) { return __uint_as_float(p.qkv_bf16 ? raw << 16 : raw); };
     auto load_rows = [&](int64_t t, const void *colsrc, Rows &x) {
         const size_t base = ((size_t)t * p.HV + hv) * K;
 #pragma unroll
@@ -168,7 +170,9 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
             x.a[i] = p.t_a[base + r];
         }
         x.b = p.t_b[t * p.HV + hv];
-        x.col = ldf(colsrc, (t * p.HV + hv) * V + col, p.qkv_bf16);
+        const int64_t ci = (t * p.HV + hv) * V + col;
+        if (p.qkv_bf16) x.col = static_cast<const uint16_t *>(colsrc)[ci];
+        else x.col = __float_as_uint(static_cast<const float *>(colsrc)[ci]);
     };
     auto load_start = [&](int c, float (&dst)[NR]) {  // state chunk c starts from
         const float *hc = p.states + ((size_t)(first_chunk + c) * p.HV + hv) * K * V;
@@ -233,7 +237,7 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
                         Spn[i] = tl - 1 > 0 ? scv[((size_t)(tl - 2) * K + rg + kRowGroups * i) * kSlice + j] : S0[i];
                     wn = swv[(tl - 1) * kSlice + j];
                 }
-                doj = cur.col;
+                doj = colval(cur.col);
                 const size_t pbase = ((size_t)slice * p.Ttot + t) * p.HV + hv;
                 part = 0.f;
 #pragma unroll
@@ -255,7 +259,7 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
             if (role == 1 && st < lr) {
                 float u = 0.f;
                 for (int g = 0; g < kRoleThreads / 64; ++g) u += red[1][parity][g][j];
-                const float wv = cur.col - u;
+                const float wv = colval(cur.col) - u;
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
                     S[i] += cur.b * cur.k[i] * wv;
