@@ -3,11 +3,12 @@
 // initial-state gradients of L = <do, o> + <dht, final_state>.
 //
 // A first, token-level form.  The forward runs first and keeps the state each chunk
-// starts from (the same kernels as the forward entry, with intermediate states).  Then
-// one workgroup per (sequence, value head, 16-column slice of V) walks its chunks last
-// to first: it recomputes the chunk's token states from the chunk-start state, then
-// takes the reverse token step (per token, with P = Diag(alpha) S_prev, u = P^T k^,
-// w = v - u, S = P + b k^ w^T):
+// starts from (the same kernels as the forward entry, with intermediate states), and a
+// parallel pre-pass forms every token's q^, k^, exp(g') and b.  Then one workgroup per
+// (sequence, value head, 16-column slice of V) walks its chunks last to first: half of
+// it recomputes the next chunk's token states from that chunk's start state while the
+// other half takes the reverse token steps of the current chunk (per token, with
+// P = Diag(alpha) S_prev, u = P^T k^, w = v - u, S = P + b k^ w^T):
 //   dS += q^ do^T;   dq^ = S do;   c = dS^T k^;   e = b c;   dv = e;   db = w . c;
 //   dk^ = b dS w - P e;   dP = dS - k^ e^T;   dg' = rowsum(dP o P);   dS <- Diag(alpha) dP
 // The sums over V (dq^, dk^, dg', db) are written per slice and added by the finishing
