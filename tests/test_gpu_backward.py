@@ -28,6 +28,9 @@ CASES = [
     TRAINING_BF16.replace(name="bwd_softplus_bf16", T=130, H=1, HV=2, K=64, V=32, safe_gate=False, lower_bound=None),
     TRAINING_BF16.replace(name="bwd_k256_bf16", T=70, H=1, HV=1, K=256, V=64),
     LONG_BF16.replace(name="bwd_pregated_negeig", T=100, H=1, HV=2, K=64, V=64),
+    VARLEN_BF16.replace(name="bwd_varlen_c32_k96_v32", num_seqs=3, min_len=20, max_len=90, H=1, HV=3, K=96, V=32,
+                        chunk=32),
+    TINY_FP32.replace(name="bwd_fp32_gva3_k32", T=77, H=1, HV=3, K=32, V=96, h0="normal0.1"),
 ]
 
 
