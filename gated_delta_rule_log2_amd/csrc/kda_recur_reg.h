@@ -227,6 +227,10 @@ recur_reg_kernel(Params p) {
             read_w(o, 0);
             read_k(o, 0);
         }
+        // step 0's W/U slot is the one the loaders refill first (with step 3): the reads
+        // above complete before the barrier that lets them start
+        wait_lgkmcnt<0>();
+        __syncthreads();
         auto step = [&](int k, auto next_tag) {
             constexpr bool has_next = decltype(next_tag)::value;
             uint4 *xs = ex_s(k & 1, j), *xv = ex_v(k & 1, j);
@@ -358,6 +362,7 @@ recur_reg_kernel(Params p) {
         QA qa[3];
         if (nsteps > 0) load_qa(qa[0], 0);
         if (nsteps > 1) load_qa(qa[1], 1);
+        __syncthreads();  // the state waves' ring prologue (no hand-over yet)
         auto iter = [&](int m, QA &buf) {
             __syncthreads();
             if (m >= 1) out_step(buf, m - 1);
@@ -375,7 +380,8 @@ recur_reg_kernel(Params p) {
         // Iteration k (after barrier k) issues W/U and KgT/d of step k + 3, then waits until
         // only those are outstanding, so what iteration k - 1 issued (step k + 2) has landed
         // before barrier k + 1, one step before the state waves start reading it.  The
-        // prologue issues steps 0..2 and waits for all but step 2.
+        // prologue issues steps 0..2 and waits for all but step 2; barrier 0 comes after the
+        // state waves have read step 0's operands, since step 3 refills step 0's W/U slot.
         const int i = wid - 4;
         auto issue_w = [&](int k) {
             if (k >= nsteps) return;
@@ -401,8 +407,9 @@ recur_reg_kernel(Params p) {
             issue_k(k);
         }
         wait_all_but(2);
+        __builtin_amdgcn_s_barrier();  // steps 0 and 1 landed; the state waves now read step 0
         for (int k = 0; k <= nsteps; ++k) {
-            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();  // k = 0: step 0's operands are in registers
             issue_w(k + 3);
             issue_k(k + 3);
             wait_all_but(k + 3);
