@@ -8,9 +8,15 @@ HBM) bracketed by device synchronisation, then K more calls of
 kda_chunk_fwd_profiled for per-kernel durations, and prints one JSON line:
   value         tokens per second of the whole job (Mtokens/s), tokens = B*T per call,
                 from the K plain calls
-  roofline      the dominant kernel's achieved algorithmic bandwidth against the
-                8 TB/s HBM peak, from HIP events recorded around every stage of the
-                second K calls on the library's stream
+  roofline      the call's algorithmic bytes (every input read once, every output
+                written once) over the measured time of the whole call, against the
+                8 TB/s HBM peak; traffic = the calibrated rocprofv3 counter bytes of
+                one call when profiles/traffic.json matches the kernel sources
+  path.stages   per kernel: HIP-event time, its algorithmic matrix FLOPs as a fraction
+                of the 2.5 PFLOP/s bf16 peak, its counter bytes and rate
+  timing        median single-call time warm and cold (512 MiB written before each
+                cold call, which evicts the memory-side cache)
+  gate_cumsum   kda_gate_chunk_cumsum on the same workload: achieved HBM GB/s
   cpu_baseline  the float64 oracle on the host cores, same workload
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -64,6 +70,32 @@ def algorithmic_flops(w, inp) -> int:
     per_chunk = NC * (NC + 1) * BC * BC * (3 * K + 2 * V) + 6 * C * K * V + C ** 3 // 3
     chunks = sum(math.ceil(L / C) for L in inp["seq_lens"])
     return int(per_chunk * chunks * HV)
+
+
+def stage_flops(w, inp) -> dict:
+    """Algorithmic matrix FLOPs of each forward stage (the split of algorithmic_flops):
+    intra forms Aqk, Akk0 (causal 16x16 tiles), W = A X, U = A v (lower-triangular A,
+    16-row blocks) and the solve; the recurrence forms W S, KgT V_new, Qg S and the
+    causal Aqk V_new."""
+    K, V, C = w.K, w.V, w.chunk
+    HV = inp["v"].shape[2]
+    NC, BC = C // 16, 16
+    chunks = sum(math.ceil(L / C) for L in inp["seq_lens"]) * HV
+    tri = NC * (NC + 1) * BC * BC
+    return {"intra": int(chunks * (tri * (3 * K + V) + C ** 3 // 3)),
+            "recurrence": int(chunks * (6 * C * K * V + tri * V)),
+            "plan": 0}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class Hip:
@@ -122,6 +154,25 @@ def load_traffic(kernel: str, per_launch_bytes_alg: float):
     if not entry or t.get("source_digest") != source_digest():
         return None
     return int(entry["fetch_kib"] * 1024 * t["copy_factor_fetch"] + entry["write_kib"] * 1024 * t["copy_factor_write"])
+
+
+def load_call_traffic(names):
+    """HBM bytes of one whole call (every stage's kernel) from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    total = 0
+    for n in names:
+        e = t.get("kernels", {}).get(n)
+        if e is None:
+            continue
+        total += e["fetch_kib"] * 1024 * t["copy_factor_fetch"] + e["write_kib"] * 1024 * t["copy_factor_write"]
+    return int(total) if total else None
 
 
 def bench_recurrent(args, w, inp, d, desc, o, ht, stream, lib, hip):
@@ -285,9 +336,64 @@ def cpu_baseline(w, inp, kw):
     run_oracle(inp, kw, nthreads=threads)
     dt = time.perf_counter() - t0
     ntok = inp["q"].shape[0] * inp["q"].shape[1]
-    return {"value": ntok / dt / 1e6, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+    return {"value": ntok / dt / 1e6, "unit": "Mtokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"full workload ({ntok} tokens x {inp['v'].shape[2]} value heads), float64 "
                       f"token recurrence, {dt:.2f} s wall"}
+
+
+def cold_warm(fn, args_, desc, stream, hip, reps, dev):
+    """Median single-call times: warm (back-to-back, caches hold what the previous call
+    left) and cold (a 512 MiB scratch buffer written right before the call, which evicts
+    the 256 MB memory-side cache and every L2)."""
+    import torch
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    warm, cold = [], []
+    a, b = hip.event(), hip.event()
+    for cold_run in (False, True):
+        for _ in range(reps):
+            if cold_run:
+                scratch.fill_(1)
+            else:
+                assert fn(ctypes.byref(desc), *args_) == 0
+            hip.record(a, stream)
+            assert fn(ctypes.byref(desc), *args_) == 0
+            hip.record(b, stream)
+            (cold if cold_run else warm).append(hip.elapsed_ms(a, b))
+    torch.cuda.synchronize(dev)
+    med = lambda x: sorted(x)[len(x) // 2]  # noqa: E731
+    return {"warm_median_ms": round(med(warm), 5), "cold_median_ms": round(med(cold), 5), "reps": reps,
+            "cold_flush_bytes": 512 << 20}
+
+
+def gate_stage(lib, desc, d, stream, hip, dev, steps):
+    """kda_gate_chunk_cumsum on the same workload: reads g (plus A_log, dt_bias), writes
+    the fp32 cumulative gate; its achieved HBM rate against the 8 TB/s peak."""
+    import torch
+
+    B, T, HV, K = d["g"].shape
+    cum = torch.empty((B, T, HV, K), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    assert lib.kda_gate_chunk_cumsum_workspace_size(ctypes.byref(desc), ctypes.byref(nb)) == 0
+    ws = torch.empty(max(nb.value, 256), dtype=torch.uint8, device=dev)
+
+    def p(t):
+        return None if t is None else t.data_ptr()
+
+    ga = (p(d["g"]), p(d["A_log"]), p(d["dt_bias"]), p(d["cu_seqlens"]), None, p(cum), p(ws), ws.numel(), stream)
+    for _ in range(3):
+        assert lib.kda_gate_chunk_cumsum(ctypes.byref(desc), *ga) == 0
+    a, b = hip.event(), hip.event()
+    hip.record(a, stream)
+    for _ in range(steps):
+        assert lib.kda_gate_chunk_cumsum(ctypes.byref(desc), *ga) == 0
+    hip.record(b, stream)
+    ms = hip.elapsed_ms(a, b) / steps
+    nbytes = d["g"].numel() * d["g"].element_size() + cum.numel() * 4 + HV * K * 4 + HV * 4
+    return {"ms": round(ms, 5), "bytes": int(nbytes), "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "what": "g read once, fp32 log2 cumulative gate written once (g_act not requested)"}
 
 
 def main() -> int:
@@ -416,12 +522,22 @@ def main() -> int:
     value = ntok / (ms_per_step * 1e-3) / 1e6
     alg_bytes = algorithmic_bytes(w, inp)
     alg_flops = algorithmic_flops(w, inp)
-    dom = max(range(nst), key=lambda i: stage_ms[i])
-    t_dom = stage_ms[dom] * 1e-3
-    achieved = alg_bytes / t_dom / 1e9
+    sflops = stage_flops(w, inp)
+    # Roofline of the path: the call's algorithmic bytes over the measured time of the
+    # whole call (every stage), against the HBM peak; the MFMA fraction beside it.
+    achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(names[dom], alg_bytes),
-                "kernel": names[dom], "kernel_ms": round(stage_ms[dom], 4)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_call_traffic(names),
+                "kernel": "whole call (" + " + ".join(n for n, x in zip(names, stage_ms) if x > 0.006) + ")",
+                "kernel_ms": round(ms_per_step, 5),
+                "mfma_frac": round(alg_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    stages = {}
+    for n, x in zip(names, stage_ms):
+        tb = load_traffic(n, alg_bytes)
+        stages[n] = {"ms": round(x, 4),
+                     "mfma_frac": round(sflops.get(n, 0) / (x * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4) if x > 0 else 0.0,
+                     "counter_bytes": tb,
+                     "counter_gbs": round(tb / (x * 1e-3) / 1e9, 1) if (tb and x > 0) else None}
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -434,8 +550,10 @@ def main() -> int:
         "path": {"algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops,
                  "hbm_frac": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(alg_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                 "stages_ms": {n: round(x, 4) for n, x in zip(names, stage_ms)},
+                 "stages": stages,
                  "host_wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4)},
+        "timing": cold_warm(lib.kda_chunk_fwd, args_, desc, stream, hip, max(5, min(args.steps, 21)), dev),
+        "gate_cumsum": gate_stage(lib, desc, d, stream, hip, dev, max(5, args.steps // 2)),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, kw)

@@ -112,7 +112,7 @@ static kda_status check_desc(const kda_fwd_desc *d, Params &p) {
     p.g_bf16 = d->g_dtype == KDA_DTYPE_BF16;
     p.beta_bf16 = d->beta_dtype == KDA_DTYPE_BF16;
     p.scale = d->scale;
-    p.lower_bound_log2 = has_lb ? lb * 1.4426950408889634f : 0.f;
+    p.lower_bound = has_lb ? lb : 0.f;
     p.output_final_state = (f & KDA_OUTPUT_FINAL_STATE) ? 1 : 0;
     p.state_vk = (f & KDA_TRANSPOSE_STATE) ? 1 : 0;
     return KDA_OK;

@@ -49,18 +49,24 @@ __device__ __forceinline__ ChunkInfo chunk_info(const Params &p, int gc) {
     return ChunkInfo{tok0, (int)(rem < p.C ? rem : p.C), n};
 }
 
-// Activated gate in natural-log units for one element.  a = exp(A_log[hv]) (or 1
-// when A_log is absent with a lower bound), dtb = dt_bias[hv*K + d] (or 0).
-__device__ __forceinline__ float gate_natural(int mode, float graw, float dtb, float a, float lb) {
-    if (mode == kGatePre) return graw;
+// Activated gate g' of one element times `unit`: 1 gives natural-log units, log2(e)
+// the log2 units every chunk kernel scans (so each later decay factor is an exp2).
+// a = exp(A_log[hv]) (1 when A_log is absent with a lower bound), dtb = dt_bias[hv*K + d]
+// (0 when absent), lb = the natural-log lower bound.  Every kernel that activates the
+// gate calls this one function: the gate entry, both intra kernels, the token-by-token
+// kernel.
+//   pre-gated:  g' = g
+//   softplus:   g' = -a * softplus(g + dtb);  above 20 softplus(x) = x to e^-20 relative
+//   bounded:    g' = lb * sigmoid(a (g + dtb)), the sigmoid taken as 1 / (1 + 2^(-a log2(e) x)),
+//               which is 0 once the power overflows and never leaves [lb, 0]
+__device__ __forceinline__ float gate_act(int mode, float graw, float dtb, float a, float lb, float unit) {
+    if (mode == kGatePre) return graw * unit;
     const float x = graw + dtb;
     if (mode == kGateSoftplus) {
-        // softplus(x) = log(1 + e^x); above 20 it equals x to within e^-20 relative
         const float sp = x > 20.f ? x : log1pf(expf(x));
-        return -a * sp;
+        return -(a * unit) * sp;
     }
-    const float z = a * x;
-    return lb * (1.f / (1.f + expf(-z)));  // lb * sigmoid(z); 0 once e^-z overflows
+    return (lb * unit) * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(a * kLog2e) * x));
 }
 
 __device__ __forceinline__ float beta_act(int mode, float b) {
@@ -110,30 +116,22 @@ __device__ __forceinline__ void gate_scan_block(const Params &p, const ChunkInfo
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[kk][i] = 0.f;
     }
-    if (p.gate_mode != kGatePre) {
-        const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
-        const float lb = p.lower_bound_log2 / kLog2e;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            if (kk < nkk) {
-                float dtb[8];
-                if (p.dt_bias) load8(p.dt_bias + (int64_t)hv * K + 32 * kk + 8 * cg, dtb);
-                else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) dtb[i] = 0.f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) G[kk][i] = valid ? gate_natural(p.gate_mode, G[kk][i], dtb[i], a, lb) : 0.f;
-            }
-        }
-    }
+    const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
+    const float lb = p.lower_bound;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         if (kk < nkk) {
+            float dtb[8];
+            if (p.dt_bias && p.gate_mode != kGatePre) load8(p.dt_bias + (int64_t)hv * K + 32 * kk + 8 * cg, dtb);
+            else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dtb[i] = 0.f;
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                gact[kk][i] = G[kk][i];
-                G[kk][i] = row_scan16(G[kk][i] * kLog2e);
+                const float x = G[kk][i];
+                gact[kk][i] = valid ? gate_act(p.gate_mode, x, dtb[i], a, lb, 1.f) : 0.f;
+                G[kk][i] = row_scan16(valid ? gate_act(p.gate_mode, x, dtb[i], a, lb, kLog2e) : 0.f);
             }
         }
     }

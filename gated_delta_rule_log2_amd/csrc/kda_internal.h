@@ -21,7 +21,7 @@ struct Params {
     int32_t gate_mode, beta_mode, qk_l2norm;
     int32_t qkv_bf16, g_bf16, beta_bf16;
     float scale;
-    float lower_bound_log2;        // lower_bound * log2(e): the bounded gate directly in log2 units
+    float lower_bound;             // natural-log lower bound of the bounded gate (0 without one)
     int32_t output_final_state;
     int32_t state_vk;              // state tensors stored [V][K] (else [K][V]) per (sequence, head)
     // inputs

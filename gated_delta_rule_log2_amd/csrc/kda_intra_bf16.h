@@ -238,37 +238,24 @@ __global__ void __launch_bounds__(C / 16 * 64) KDA_INTRA_OCC intra_bf16_kernel(P
         }
     }
 
-    // ---- step 1: activated gate in log2 units, 16-row inclusive scan ----
-    if (p.gate_mode == kGateLowerBound) {
-        // lower_bound * sigmoid(exp(A_log) (g + dt_bias)); sigmoid(z) = 1 / (1 + 2^(-z log2 e))
-        const float aL = (p.A_log ? expf(p.A_log[hv]) : 1.f) * kLog2e;
-        const float lb = valid ? p.lower_bound_log2 : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const float dtb[8] = {dtbv[kk][0].x, dtbv[kk][0].y, dtbv[kk][0].z, dtbv[kk][0].w,
-                                  dtbv[kk][1].x, dtbv[kk][1].y, dtbv[kk][1].z, dtbv[kk][1].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float z = (G[kk][i] + dtb[i]) * aL;
-                G[kk][i] = lb * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z));
-            }
-        }
-    } else if (p.gate_mode == kGateSoftplus) {
+    // ---- step 1: activated gate in log2 units (rows past the end contribute 0), 16-row
+    //      inclusive scan; one loop per gate form so the element loop has no branch ----
+    {
         const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
-        const float s = valid ? kLog2e : 0.f;
+        const float unit = valid ? kLog2e : 0.f;
+        auto act = [&](auto mode_tag) {
+            constexpr int M = decltype(mode_tag)::value;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const float dtb[8] = {dtbv[kk][0].x, dtbv[kk][0].y, dtbv[kk][0].z, dtbv[kk][0].w,
-                                  dtbv[kk][1].x, dtbv[kk][1].y, dtbv[kk][1].z, dtbv[kk][1].w};
+            for (int kk = 0; kk < NKK; ++kk) {
+                const float dtb[8] = {dtbv[kk][0].x, dtbv[kk][0].y, dtbv[kk][0].z, dtbv[kk][0].w,
+                                      dtbv[kk][1].x, dtbv[kk][1].y, dtbv[kk][1].z, dtbv[kk][1].w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) G[kk][i] = s * gate_natural(kGateSoftplus, G[kk][i], dtb[i], a, 0.f);
-        }
-    } else {
-        const float s = valid ? kLog2e : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) G[kk][i] *= s;
+                for (int i = 0; i < 8; ++i) G[kk][i] = gate_act(M, G[kk][i], dtb[i], a, p.lower_bound, unit);
+            }
+        };
+        if (p.gate_mode == kGateLowerBound) act(std::integral_constant<int, kGateLowerBound>{});
+        else if (p.gate_mode == kGateSoftplus) act(std::integral_constant<int, kGateSoftplus>{});
+        else act(std::integral_constant<int, kGatePre>{});
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(kRecThreads) fused_recurrent_kernel(Params p) 
     for (int i = 0; i < RPT; ++i) S[i] = p.h0 ? p.h0[sidx(d0 + i)] : 0.f;
 
     const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
-    const float lb = p.lower_bound_log2 / kLog2e;  // natural-log lower bound
+    const float lb = p.lower_bound;  // natural-log lower bound
     const float dtb = (p.dt_bias && tid < K) ? p.dt_bias[(int64_t)hv * K + tid] : 0.f;
 
     // raw inputs of one token: channel tid of q, k and the gate; column tid of the v slice;
@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(kRecThreads) fused_recurrent_kernel(Params p) 
         if (tid < K) {
             qs[tid] = qr;
             ks[tid] = kr;
-            als[tid] = __builtin_amdgcn_exp2f(gate_natural(p.gate_mode, gr, dtb, a, lb) * kLog2e);
+            als[tid] = __builtin_amdgcn_exp2f(gate_act(p.gate_mode, gr, dtb, a, lb, kLog2e));
             q2 = qr * qr;
             k2 = kr * kr;
         }

@@ -54,7 +54,8 @@ typedef enum kda_status {
     KDA_ERR_SHAPE = 2,          /* a size is negative or zero where it must be positive, or too large */
     KDA_ERR_CHUNK_SIZE = 3,     /* chunk_size not 32 or 64 ([ENG] §2.1) */
     KDA_ERR_HEAD_DIM = 4,       /* K > 256 ([ENG] §2.1) */
-    KDA_ERR_UNSUPPORTED = 5,    /* build limit: K not a multiple of 32, V not a multiple of 16, V > 256 */
+    KDA_ERR_UNSUPPORTED = 5,    /* build limit: K or V not a multiple of 32, V > 256, fp32 q/k/v with
+                                   K = V = 256 (over one CU's 160 KB of LDS), or an unknown flag bit */
     KDA_ERR_GVA = 6,            /* HV is not a multiple of H ([ENG] §2.1) */
     KDA_ERR_MISSING_A_LOG = 7,  /* in-kernel gate without lower bound needs A_log ([ENG] §2.1) */
     KDA_ERR_LOWER_BOUND = 8,    /* safe gate needs -5 <= lower_bound < 0; any bound must be < 0 ([ENG] §2.1) */
@@ -116,9 +117,12 @@ int kda_abi_version(void);
 const char *kda_status_string(kda_status s);
 
 /*
- * Bytes of device workspace kda_chunk_fwd needs for this descriptor.  Runs the
- * same descriptor checks as kda_chunk_fwd (no device pointers involved) and
- * writes *bytes only on KDA_OK.  Host only; no HIP call.
+ * Bytes of device workspace kda_chunk_fwd needs for this descriptor.  The caller
+ * allocates the workspace and passes it in, as FlashKDA's Python layer allocates the
+ * workspace its kernels use ("FlashKDA gate偏置加載路徑完整解析…", §二 第1段); the
+ * library itself never allocates.  Runs the same descriptor checks as kda_chunk_fwd
+ * (no device pointers involved) and writes *bytes only on KDA_OK.  Host only; no HIP
+ * call.
  */
 kda_status kda_chunk_fwd_workspace_size(const kda_fwd_desc *d, size_t *bytes);
 
@@ -265,7 +269,10 @@ kda_status kda_gate_chunk_cumsum_workspace_size(const kda_fwd_desc *d, size_t *b
 /*
  * Gate activation fused with the chunk-local cumulative sum ([ENG] §2, the fused
  * "activation + in-chunk cumsum" kernel; [NOTES] forward step 1), exported on
- * its own for inspection.  The same device code feeds kda_chunk_fwd.
+ * its own for inspection.  The activation is the one device function the bf16 and
+ * fp32 intra kernels of kda_chunk_fwd also call (gate_act in kda_gate.h); the
+ * cumulative sum here runs over whole chunks, while inside kda_chunk_fwd the bf16
+ * kernel scans 16-row sub-chunks and adds the earlier sub-chunks' totals per column.
  *
  *   g           [B, T, HV, K]  g_dtype (raw with KDA_GATE_IN_KERNEL, else pre-gated)
  *   A_log, dt_bias, cu_seqlens  as for kda_chunk_fwd

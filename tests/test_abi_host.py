@@ -82,6 +82,8 @@ CASES = [
     ("K = 512 (the pages' literal example)", dict(K=512, V=512), "KDA_ERR_HEAD_DIM"),
     ("K not a multiple of 32", dict(K=80), "KDA_ERR_UNSUPPORTED"),
     ("V > 256", dict(V=288), "KDA_ERR_UNSUPPORTED"),
+    ("V not a multiple of 32", dict(V=48), "KDA_ERR_UNSUPPORTED"),
+    ("fp32 K = V = 256 (over one CU's LDS)", dict(K=256, V=256, qkv_dtype=_abi.DTYPE_FP32), "KDA_ERR_UNSUPPORTED"),
     ("HV % H != 0", dict(H=3, HV=4), "KDA_ERR_GVA"),
     ("safe gate without lower bound", dict(flags=_abi.SAFE_GATE | _abi.GATE_IN_KERNEL), "KDA_ERR_LOWER_BOUND"),
     ("safe gate lb = -6", dict(flags=_abi.SAFE_GATE | _abi.HAS_LOWER_BOUND, lower_bound=-6.0), "KDA_ERR_LOWER_BOUND"),
