@@ -33,8 +33,9 @@ EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
     "kda_gate_chunk_cumsum_workspace_size", "kda_gate_chunk_cumsum", "kda_chunk_fwd_stage_count",
     "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd", "kda_chunk_fwd_states",
-    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaFwdDesc(ctypes.Structure):
@@ -88,6 +89,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_stage_count.restype = ctypes.c_int
     lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
     lib.kda_fused_recurrent_fwd.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.kda_chunk_fwd_stage_count.argtypes = []
     lib.kda_chunk_fwd_stage_name.restype = ctypes.c_char_p
     lib.kda_chunk_fwd_stage_name.argtypes = [ctypes.c_int]

@@ -21,7 +21,7 @@ SOURCES = [
     "kda_abi.cpp", "kda_dispatch.hip", "kda_plan_gate.hip",
     "kda_intra_c64_bf16.hip", "kda_intra_c64_f32.hip", "kda_intra_c32_bf16.hip", "kda_intra_c32_f32.hip",
     "kda_recur_c64_bf16.hip", "kda_recur_c64_f32.hip", "kda_recur_c32_bf16.hip", "kda_recur_c32_f32.hip",
-    "kda_recurrent.hip", "kda_backward.hip",
+    "kda_recurrent.hip", "kda_backward.hip", "kda_noalloc.hip",
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -178,7 +178,7 @@ const char *kda_chunk_fwd_stage_name(int i) { return (i >= 0 && i < kNumStages) 
 // The whole forward: checks, then plan -> intra -> recurrence on `stream`.  `states`
 // (the state each chunk starts from) is written when want_states; `ev` as for
 // kda_chunk_fwd_profiled.
-static kda_status chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                             const int64_t *cu_seqlens, void *o, float *final_state, bool want_states,
                             float *states, void *workspace, size_t workspace_bytes, hipStream_t stream,
@@ -221,7 +221,7 @@ kda_status kda_chunk_fwd_profiled(const kda_fwd_desc *d, const void *q, const vo
                                   const float *initial_state, const int64_t *cu_seqlens, void *o,
                                   float *final_state, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream, hipEvent_t *ev) {
-    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
+    return chunk_fwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
                      nullptr, workspace, workspace_bytes, stream, ev);
 }
 
@@ -230,7 +230,7 @@ kda_status kda_chunk_fwd(const kda_fwd_desc *d, const void *q, const void *k, co
                          const float *initial_state, const int64_t *cu_seqlens, void *o,
                          float *final_state, void *workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
+    return chunk_fwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, false,
                      nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -239,7 +239,7 @@ kda_status kda_chunk_fwd_states(const kda_fwd_desc *d, const void *q, const void
                                 const float *initial_state, const int64_t *cu_seqlens, void *o,
                                 float *final_state, float *states, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-    return chunk_fwd(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, true,
+    return chunk_fwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, true,
                      states, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -377,7 +377,7 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, co
     // forward with the chunk-start states (its output o is not needed)
     kda_fwd_desc fd = *d;
     fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
-    st = chunk_fwd(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
+    st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
                    states, workspace, FL.total_bytes, stream, nullptr);
     if (st != KDA_OK) return st;
 

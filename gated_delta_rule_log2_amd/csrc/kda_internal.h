@@ -60,3 +60,14 @@ hipError_t launch_recurrence(const Params &p, hipStream_t s);
 hipError_t launch_fused_recurrent(const Params &p, hipStream_t s);
 
 }  // namespace kda
+
+#include "../../include/kda.h"
+
+namespace kda {
+// The forward of kda_chunk_fwd / _states / _profiled: descriptor, pointer and workspace
+// checks, then plan -> intra -> recurrence on `stream` (kda_abi.cpp).
+kda_status chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                         const int64_t *cu_seqlens, void *o, float *final_state, bool want_states, float *states,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev);
+}  // namespace kda

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -235,6 +235,34 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d,
                          float *dq, float *dk, float *dv, float *dg, float *dbeta,
                          float *dA_log, float *ddt_bias, float *dh0,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: kda_chunk_fwd with its
+ * workspace taken from a fixed device array inside the library, so the call itself
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * Arguments, layouts, flags, checks and results are those of kda_chunk_fwd, without
+ * the workspace arguments; o and final_state are bit for bit those of kda_chunk_fwd.
+ *   - The array holds KDA_NOALLOC_SCRATCH_BYTES; a descriptor whose
+ *     kda_chunk_fwd_workspace_size exceeds it returns KDA_ERR_WORKSPACE before
+ *     anything is enqueued (for K = V = 128, chunk 64: up to 904 (chunk, value head)
+ *     pairs per call, e.g. 1 792 tokens at 32 value heads).
+ *   - Every GPU the library runs on holds its own copy of the array from module load
+ *     until the process ends.  The first call on a device looks up its device address
+ *     once (hipGetSymbolAddress, with that device current); KDA_ERR_HIP if that fails.
+ *   - `stream` must belong to the current device.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents (no call reads contents it did not write itself).  Calls on one stream
+ *     are ordered and safe; calls that overlap on one GPU (different streams, or
+ *     threads without ordering) race.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_fwd_desc *d,
+                                 const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, const float *A_log, const float *dt_bias,
+                                 const float *initial_state, const int64_t *cu_seqlens,
+                                 void *o, float *final_state, hipStream_t stream);
 
 /*
  * Stage introspection for profiling.  kda_chunk_fwd enqueues
