@@ -131,11 +131,12 @@ class Hip:
 
 def source_digest() -> str:
     """Digest of the forward path's sources: every file under csrc/ except the backward's
-    own kernels (kda_backward.*), which the forward's kernels neither include nor launch."""
+    own kernels (kda_backward.*, kda_bwd_*), which the forward's kernels neither include nor
+    launch."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_log2_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("kda_backward."):
+        if name.startswith(("kda_backward.", "kda_bwd_")):
             continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())

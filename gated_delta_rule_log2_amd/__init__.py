@@ -244,12 +244,17 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   use_gate_in_kernel: bool = False, safe_gate: bool = False,
                   lower_bound: Optional[float] = None, A_log: Optional[torch.Tensor] = None,
                   dt_bias: Optional[torch.Tensor] = None, use_beta_sigmoid_in_kernel: bool = False,
-                  allow_neg_eigval: bool = False, *, workspace: Optional[torch.Tensor] = None) -> dict:
+                  allow_neg_eigval: bool = False, *, workspace: Optional[torch.Tensor] = None,
+                  tokenwise: bool = False) -> dict:
     """Gradients of <do, o> + <dht, final_state> for chunk_kda's inputs, on the current
     HIP stream (the forward is recomputed inside).  Arguments as chunk_kda; do has o's
     shape and dtype, dht the final state's ([N, HV, K, V] float32) or None.  Returns
     float32 tensors in a dict: dq, dk, dv, dg, dbeta, and dA_log / dt_bias / dh0 for
     the inputs given (dh0 always: the gradient at the initial state, zero or given).
+    tokenwise=True runs the token-level form (kda_chunk_bwd_tokenwise) instead of the
+    chunked one.  The workspace is allocated per call from torch's caching allocator
+    (stream-ordered, so it is reused once the call's work is done) unless one is given;
+    the forward's cached workspace is never grown by a backward call.
     """
     lib = library()
     B, T, H, K = q.shape
@@ -273,12 +278,13 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     _check_tensor(dht, "dht", (N, HV, K, V), dev, torch.float32)
     cu_dev = None if cu_seqlens is None else cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
     nbytes = ctypes.c_size_t(0)
-    rc = lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc.d), ctypes.byref(nbytes))
+    size_fn = lib.kda_chunk_bwd_tokenwise_workspace_size if tokenwise else lib.kda_chunk_bwd_workspace_size
+    rc = size_fn(ctypes.byref(desc.d), ctypes.byref(nbytes))
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
     stream = torch.cuda.current_stream(dev).cuda_stream
     if workspace is None:
-        workspace = _workspace(dev, stream, nbytes.value)
+        workspace = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
            "dv": torch.empty((B, T, HV, V), **f32), "dg": torch.empty((B, T, HV, K), **f32),
@@ -287,7 +293,8 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         out["dA_log"] = torch.empty((HV,), **f32)
     if dt_bias is not None:
         out["ddt_bias"] = torch.empty((HV * K,), **f32)
-    rc = lib.kda_chunk_bwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+    run = lib.kda_chunk_bwd_tokenwise if tokenwise else lib.kda_chunk_bwd
+    rc = run(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
                            _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(do), _ptr(dht),
                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                            _ptr(out["dbeta"]), _ptr(out.get("dA_log")), _ptr(out.get("ddt_bias")),

@@ -22,6 +22,7 @@ SOURCES = [
     "kda_intra_c64_bf16.hip", "kda_intra_c64_f32.hip", "kda_intra_c32_bf16.hip", "kda_intra_c32_f32.hip",
     "kda_recur_c64_bf16.hip", "kda_recur_c64_f32.hip", "kda_recur_c32_bf16.hip", "kda_recur_c32_f32.hip",
     "kda_recurrent.hip", "kda_backward.hip", "kda_noalloc.hip",
+    "kda_bwd_chunk_bf16.hip", "kda_bwd_chunk_f32.hip",
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -292,17 +292,24 @@ namespace {
 
 struct BwdLayout {
     size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
-        off_ta, off_tb, off_param, total;
+        off_ta, off_tb, off_param, off_du, off_dh, total;
+    int nslices;
 };
 
 // After the forward's own workspace: the chunk-start states, the forward output (not
-// returned), the per-slice partial sums and the per-workgroup token-state scratch.
-BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
+// returned), the per-element partial sums the finishing kernels add, and the scratch of
+// the form in use.  The chunked form keeps one partial sum per element plus dU and the
+// per-chunk state gradients; the token-level form one partial sum per 16-column slice of
+// V plus its per-token operands and token-state scratch.
+BwdLayout bwd_layout(const Params &p, size_t fwd_bytes, bool chunked) {
     BwdLayout L{};
-    const size_t Ttot = (size_t)p.B * p.T, ns = (size_t)bwd_slices(p.V), f = sizeof(float);
+    const size_t Ttot = (size_t)p.B * p.T, f = sizeof(float);
+    const size_t ns = chunked ? 1 : (size_t)bwd_slices(p.V);
+    const size_t slots = (size_t)p.total_chunks * p.HV;
+    L.nslices = (int)ns;
     size_t off = align256(fwd_bytes);
     L.off_states = off;
-    off = align256(off + f * (size_t)p.total_chunks * p.HV * p.K * p.V);
+    off = align256(off + f * slots * p.K * p.V);
     L.off_o = off;
     off = align256(off + (p.qkv_bf16 ? 2 : 4) * Ttot * p.HV * p.V);
     L.off_pdq = off;
@@ -313,22 +320,29 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes) {
     off = align256(off + f * ns * Ttot * p.HV * p.K);
     L.off_pdb = off;
     off = align256(off + f * ns * Ttot * p.HV);
-    const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
-    L.off_sstate = off;
-    off = align256(off + f * scr);
-    L.off_sw = L.off_sstate + f * bwd_seq_state_floats(p.N, p.HV, p.K, p.V, p.C);
     L.off_da = off;
     off = align256(off + f * Ttot * p.HV * p.K);
-    L.off_tq = off;
-    off = align256(off + f * Ttot * p.HV * p.K);
-    L.off_tk = off;
-    off = align256(off + f * Ttot * p.HV * p.K);
-    L.off_ta = off;
-    off = align256(off + f * Ttot * p.HV * p.K);
-    L.off_tb = off;
-    off = align256(off + f * Ttot * p.HV);
     L.off_param = off;
     off = align256(off + f * bwd_param_scratch_floats(p.HV, p.K));
+    if (chunked) {
+        L.off_du = off;
+        off = align256(off + f * slots * p.C * p.V);
+        L.off_dh = off;
+        off = align256(off + f * slots * p.K * p.V);
+    } else {
+        const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
+        L.off_sstate = off;
+        off = align256(off + f * scr);
+        L.off_sw = L.off_sstate + f * bwd_seq_state_floats(p.N, p.HV, p.K, p.V, p.C);
+        L.off_tq = off;
+        off = align256(off + f * Ttot * p.HV * p.K);
+        L.off_tk = off;
+        off = align256(off + f * Ttot * p.HV * p.K);
+        L.off_ta = off;
+        off = align256(off + f * Ttot * p.HV * p.K);
+        L.off_tb = off;
+        off = align256(off + f * Ttot * p.HV);
+    }
     L.total = off;
     return L;
 }
@@ -340,25 +354,21 @@ kda_status bwd_check(const kda_fwd_desc *d, Params &p) {
     return KDA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
+kda_status bwd_workspace(const kda_fwd_desc *d, size_t *bytes, bool tokenwise) {
     Params p;
     kda_status st = bwd_check(d, p);
     if (st != KDA_OK) return st;
     if (!bytes) return KDA_ERR_NULL_POINTER;
     const size_t fwd = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4).total_bytes;
-    *bytes = bwd_layout(p, fwd).total;
+    *bytes = bwd_layout(p, fwd, !tokenwise && bwd_chunk_fits(p.K)).total;
     return KDA_OK;
 }
 
-kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
-                         const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk,
-                         float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                   const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                   const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk, float *dv,
+                   float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream, bool tokenwise) {
     Params p;
     kda_status st = bwd_check(d, p);
     if (st != KDA_OK) return st;
@@ -368,17 +378,19 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, co
     if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
         return KDA_ERR_MISSING_A_LOG;
     if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    const bool chunked = !tokenwise && bwd_chunk_fits(p.K);
     const WorkspaceLayout FL = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4);
-    const BwdLayout L = bwd_layout(p, FL.total_bytes);
+    const BwdLayout L = bwd_layout(p, FL.total_bytes, chunked);
     if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     float *states = reinterpret_cast<float *>(ws + L.off_states);
 
-    // forward with the chunk-start states (its output o is not needed)
+    // backward steps 1-2: the forward with the state each chunk starts from (its output o
+    // is not needed); its per-chunk intermediates stay in the workspace
     kda_fwd_desc fd = *d;
     fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
     st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
-                   states, workspace, FL.total_bytes, stream, nullptr);
+                       states, workspace, FL.total_bytes, stream, nullptr);
     if (st != KDA_OK) return st;
 
     BwdParams b{};
@@ -394,19 +406,65 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, co
     b.dA_log = A_log ? dA_log : nullptr;
     b.ddt_bias = dt_bias ? ddt_bias : nullptr;
     b.dh0 = dh0;
+    b.nslices = L.nslices;
     b.p_dq = reinterpret_cast<float *>(ws + L.off_pdq);
     b.p_dk = reinterpret_cast<float *>(ws + L.off_pdk);
     b.p_dg = reinterpret_cast<float *>(ws + L.off_pdg);
     b.p_db = reinterpret_cast<float *>(ws + L.off_pdb);
-    b.scr_state = reinterpret_cast<float *>(ws + L.off_sstate);
-    b.scr_w = reinterpret_cast<float *>(ws + L.off_sw);
     b.scr_da = reinterpret_cast<float *>(ws + L.off_da);
-    b.t_q = reinterpret_cast<float *>(ws + L.off_tq);
-    b.t_k = reinterpret_cast<float *>(ws + L.off_tk);
-    b.t_a = reinterpret_cast<float *>(ws + L.off_ta);
-    b.t_b = reinterpret_cast<float *>(ws + L.off_tb);
     b.scr_param = reinterpret_cast<float *>(ws + L.off_param);
-    return to_status(launch_backward(b, stream));
+    if (!chunked) {
+        b.scr_state = reinterpret_cast<float *>(ws + L.off_sstate);
+        b.scr_w = reinterpret_cast<float *>(ws + L.off_sw);
+        b.t_q = reinterpret_cast<float *>(ws + L.off_tq);
+        b.t_k = reinterpret_cast<float *>(ws + L.off_tk);
+        b.t_a = reinterpret_cast<float *>(ws + L.off_ta);
+        b.t_b = reinterpret_cast<float *>(ws + L.off_tb);
+        return to_status(launch_backward(b, stream));
+    }
+    // backward steps 3-7: the reverse chunk recurrence, the per-chunk gradients, then the
+    // chain rules of the input transforms
+    BwdChunkParams P{};
+    P.f = p;
+    P.f.q = q; P.f.k = k; P.f.v = v; P.f.g = g; P.f.beta = beta;
+    P.f.A_log = A_log; P.f.dt_bias = dt_bias; P.f.h0 = initial_state; P.f.cu_seqlens = cu_seqlens;
+    bind_workspace(P.f, workspace, FL);
+    P.b = b;
+    P.dU = reinterpret_cast<float *>(ws + L.off_du);
+    P.dh = reinterpret_cast<float *>(ws + L.off_dh);
+    hipError_t e = launch_bwd_dhu(P, stream);
+    if (e == hipSuccess) e = launch_bwd_local(P, stream);
+    if (e == hipSuccess) e = launch_bwd_finish(b, stream);
+    return to_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes) { return bwd_workspace(d, bytes, false); }
+
+kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                         const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk,
+                         float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return bwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta,
+                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, false);
+}
+
+kda_status kda_chunk_bwd_tokenwise_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
+    return bwd_workspace(d, bytes, true);
+}
+
+kda_status kda_chunk_bwd_tokenwise(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *A_log, const float *dt_bias,
+                                   const float *initial_state, const int64_t *cu_seqlens, const void *dout,
+                                   const float *dht, float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                                   float *dA_log, float *ddt_bias, float *dh0, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return bwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta,
+                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

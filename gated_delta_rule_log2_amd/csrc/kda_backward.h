@@ -28,7 +28,23 @@ struct BwdParams {
     float *t_q, *t_k, *t_a;         // [Ttot, HV, K] q^, k^ (of the head's qk head), exp(g')
     float *t_b;                     // [Ttot, HV] beta after its transform
     float *scr_param;               // [HV, 64, K + 1] per-segment dt_bias / A_log sums
+    int32_t nslices;                // partial sums per element in p_dq, p_dk, p_dg, p_db (summed in order)
 };
+
+// The chunked backward's kernels see the forward's parameters (chunk plan, the per-chunk
+// intermediates W, Qg, KgT, Aqk, d in the forward workspace) beside the backward's.
+struct BwdChunkParams {
+    Params f;
+    BwdParams b;
+    float *dU;                      // [total chunks * HV][C][V] gradient of U - W S (dV_new)
+    float *dh;                      // [total chunks * HV][K][V] gradient of the state after each chunk
+};
+
+// The chunked backward covers K <= 128 (the token-level form above that).
+bool bwd_chunk_fits(int K);
+hipError_t launch_bwd_dhu(const BwdChunkParams &p, hipStream_t s);
+hipError_t launch_bwd_local(const BwdChunkParams &p, hipStream_t s);
+hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s);
 
 int bwd_slices(int V);
 size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C);

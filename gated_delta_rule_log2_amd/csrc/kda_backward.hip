@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
     __shared__ float ws[4][4];
     const int64_t t = blockIdx.x / p.H;
     const int h = blockIdx.x % p.H, d = threadIdx.x;
-    const int group = p.HV / p.H, ns = p.V / kSlice;
+    const int group = p.HV / p.H, ns = p.nslices;
     float gq = 0.f, gk = 0.f, qv = 0.f, kv = 0.f;
     if (d < p.K) {
         for (int jv = 0; jv < group; ++jv)
@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
 __global__ void __launch_bounds__(kBwdThreads) bwd_gate_kernel(BwdParams p) {
     const int64_t t = blockIdx.x / p.HV;
     const int hv = blockIdx.x % p.HV, d = threadIdx.x;
-    const int ns = p.V / kSlice;
+    const int ns = p.nslices;
     if (d < p.K) {
         float gp = 0.f;  // dL/dg' (natural-log activated gate)
         for (int sl = 0; sl < ns; ++sl) gp += p.p_dg[(((size_t)sl * p.Ttot + t) * p.HV + hv) * p.K + d];
@@ -460,6 +460,13 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return launch_bwd_finish(p, s);
+}
+
+// The finishing kernels shared by both backward forms: per-element partial sums
+// (p.nslices of them) -> dq, dk (GVA sum, scale and L2-norm chain rule), dg, dbeta
+// (activation chain rules), then the dt_bias and A_log token sums.
+hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s) {
     if (p.Ttot > 0) {
         hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)(p.Ttot * p.H)), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);

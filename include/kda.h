@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -206,11 +206,15 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
 /*
  * chunk_kda backward: the gradients of L = <do, o> + <dht, final_state> with respect
  * to every input of kda_chunk_fwd ("Reading Notes: Implementation Notes for KDA in
- * FLA", backward; the same operator, descriptor and input contract as kda_chunk_fwd).
- * It runs the forward first (keeping the state each chunk starts from in the
- * workspace), then walks every (sequence, value head) from its last token to its
- * first.  A first, token-level form: correct for every configuration the forward
- * accepts except KDA_TRANSPOSE_STATE (KDA_ERR_UNSUPPORTED), not tuned for speed.
+ * FLA", backward; the same operator, descriptor and input contract as kda_chunk_fwd),
+ * in the chunked form of that section's steps 1-7: the forward is recomputed with the
+ * state each chunk starts from (steps 1-2), a reverse recurrence over chunks carries the
+ * state gradient and gives dU = dL/dV_new per chunk (step 4), and one pass per (chunk,
+ * value head) forms dAqk (step 3), the WY chain (step 5), the intra-chunk terms with the
+ * gate offsets of the forward (step 6) and the suffix sum that turns cumulative-gate
+ * gradients into gate gradients (step 7).  For K > 128 the token-level form of
+ * kda_chunk_bwd_tokenwise runs instead.  KDA_TRANSPOSE_STATE is refused
+ * (KDA_ERR_UNSUPPORTED).
  *   dout     [B*T, HV, V]  dtype qkv_dtype (the dtype of o); required when B*T > 0
  *   dht      [N, HV, K, V] fp32 gradient of final_state, or NULL (zero)
  * Outputs, all fp32, fully overwritten, same layouts as the inputs:
@@ -223,8 +227,10 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
  *   dh0      [N, HV, K, V] gradient of the initial state, written when non-NULL
  *            (also without initial_state: the gradient at a zero initial state)
  * Workspace: kda_chunk_bwd_workspace_size bytes, device memory owned by the caller,
- * not retained.  Errors: those of kda_chunk_fwd, KDA_ERR_NULL_POINTER for a missing
- * dout or required output when B*T > 0.  Asynchronous on `stream`.
+ * not retained (the forward's workspace, the chunk-start states, dU and the per-chunk
+ * state gradients: 1.58 GB at B = 1, T = 8192, HV = 32, K = V = 128, bf16).  Errors: those of
+ * kda_chunk_fwd, KDA_ERR_NULL_POINTER for a missing dout or required output when
+ * B*T > 0.  Asynchronous on `stream`.  Results do not depend on scheduling (no atomics).
  */
 kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes);
 kda_status kda_chunk_bwd(const kda_fwd_desc *d,
@@ -235,6 +241,24 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d,
                          float *dq, float *dk, float *dv, float *dg, float *dbeta,
                          float *dA_log, float *ddt_bias, float *dh0,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The same gradients as kda_chunk_bwd by the token-level form: after the forward with
+ * chunk-start states, one workgroup per (sequence, value head, 16-column slice of V)
+ * takes the token recurrence's reverse steps from the last token to the first.  Every
+ * configuration kda_chunk_fwd accepts except KDA_TRANSPOSE_STATE; slower than the
+ * chunked form, and kept as an independent cross-check of it.  Arguments and errors as
+ * kda_chunk_bwd; its own workspace size.
+ */
+kda_status kda_chunk_bwd_tokenwise_workspace_size(const kda_fwd_desc *d, size_t *bytes);
+kda_status kda_chunk_bwd_tokenwise(const kda_fwd_desc *d,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *A_log, const float *dt_bias,
+                                   const float *initial_state, const int64_t *cu_seqlens,
+                                   const void *dout, const float *dht,
+                                   float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                                   float *dA_log, float *ddt_bias, float *dh0,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * For callers that cannot allocate device memory -- code under HIP graph capture,

@@ -19,6 +19,10 @@ hipError_t launch_intra(const Params &, hipStream_t) { ++g_stub_launches; return
 hipError_t launch_recurrence(const Params &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_fused_recurrent(const Params &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_backward(const BwdParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+hipError_t launch_bwd_dhu(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+hipError_t launch_bwd_local(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+hipError_t launch_bwd_finish(const BwdParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+bool bwd_chunk_fits(int K) { return K <= 128; }
 }  // namespace kda
 
 namespace kda {
