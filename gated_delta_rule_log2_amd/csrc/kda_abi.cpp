@@ -292,7 +292,7 @@ namespace {
 
 struct BwdLayout {
     size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
-        off_ta, off_tb, off_param, off_du, off_dh, total;
+        off_ta, off_tb, off_param, off_du, off_dh, off_rpack, off_ppack, off_doq, total;
     int nslices;
 };
 
@@ -329,6 +329,14 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes, bool chunked) {
         off = align256(off + f * slots * p.C * p.V);
         L.off_dh = off;
         off = align256(off + f * slots * p.K * p.V);
+        if (p.qkv_bf16) {  // the reverse recurrence's transposed operands and dO (bf16)
+            L.off_rpack = off;
+            off = align256(off + 2 * slots * 2 * p.C * p.K);
+            L.off_ppack = off;
+            off = align256(off + 2 * slots * ((size_t)p.C * p.C + (size_t)p.K * p.C));
+            L.off_doq = off;
+            off = align256(off + 2 * slots * p.V * p.C);
+        }
     } else {
         const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
         L.off_sstate = off;
@@ -432,6 +440,11 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     P.b = b;
     P.dU = reinterpret_cast<float *>(ws + L.off_du);
     P.dh = reinterpret_cast<float *>(ws + L.off_dh);
+    if (p.qkv_bf16) {
+        P.rpack = reinterpret_cast<uint16_t *>(ws + L.off_rpack);
+        P.ppack = reinterpret_cast<uint16_t *>(ws + L.off_ppack);
+        P.doq = reinterpret_cast<uint16_t *>(ws + L.off_doq);
+    }
     hipError_t e = launch_bwd_dhu(P, stream);
     if (e == hipSuccess) e = launch_bwd_local(P, stream);
     if (e == hipSuccess) e = launch_bwd_finish(b, stream);

@@ -38,6 +38,10 @@ struct BwdChunkParams {
     BwdParams b;
     float *dU;                      // [total chunks * HV][C][V] gradient of U - W S (dV_new)
     float *dh;                      // [total chunks * HV][K][V] gradient of the state after each chunk
+    // bf16 intermediates: the reverse recurrence's operands, per (chunk, value head) slot
+    uint16_t *rpack;                // Kg [C][K], W^T [K][C] (permuted row fragments)
+    uint16_t *ppack;                // Aqk^T [C][C], Qg^T [K][C] (permuted row fragments)
+    uint16_t *doq;                  // dO [V][C] in accumulator-tile order
 };
 
 // The chunked backward covers K <= 128 (the token-level form above that).

@@ -1,8 +1,28 @@
 // Chunked backward kernels for bf16 q/k/v (bf16 intermediates: bf16 matrix-core
 // operands with fp32 accumulation), chunk 32 and 64, K = 32..128.
 #include "kda_bwd_chunk.h"
+#include "kda_bwd_dhu_reg.h"
 
 namespace kda {
-hipError_t launch_bwd_dhu_bf16(const BwdChunkParams &p, hipStream_t s) { return launch_bwd_dhu_c<uint16_t>(p, s); }
+// the reverse recurrence with the state gradient in registers (bf16 intermediates)
+hipError_t launch_bwd_dhu_bf16(const BwdChunkParams &p, hipStream_t s) {
+    const int nkk = p.f.K / 32;
+    if (p.f.C == 64) {
+        switch (nkk) {
+        case 1: return launch_bwd_dhu_reg_t<64, 1>(p, s);
+        case 2: return launch_bwd_dhu_reg_t<64, 2>(p, s);
+        case 3: return launch_bwd_dhu_reg_t<64, 3>(p, s);
+        case 4: return launch_bwd_dhu_reg_t<64, 4>(p, s);
+        }
+    } else {
+        switch (nkk) {
+        case 1: return launch_bwd_dhu_reg_t<32, 1>(p, s);
+        case 2: return launch_bwd_dhu_reg_t<32, 2>(p, s);
+        case 3: return launch_bwd_dhu_reg_t<32, 3>(p, s);
+        case 4: return launch_bwd_dhu_reg_t<32, 4>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
 hipError_t launch_bwd_local_bf16(const BwdChunkParams &p, hipStream_t s) { return launch_bwd_local_c<uint16_t>(p, s); }
 }  // namespace kda
