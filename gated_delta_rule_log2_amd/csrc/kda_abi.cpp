@@ -292,15 +292,16 @@ namespace {
 
 struct BwdLayout {
     size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
-        off_ta, off_tb, off_param, off_du, off_dh, off_rpack, off_ppack, off_doq, total;
+        off_ta, off_tb, off_param, off_du, off_dh, off_cparam, off_rpack, off_ppack, off_doq, total;
     int nslices;
 };
 
 // After the forward's own workspace: the chunk-start states, the forward output (not
-// returned), the per-element partial sums the finishing kernels add, and the scratch of
-// the form in use.  The chunked form keeps one partial sum per element plus dU and the
-// per-chunk state gradients; the token-level form one partial sum per 16-column slice of
-// V plus its per-token operands and token-state scratch.
+// returned), the per-value-head partial sums of dq and dk, and the scratch of the form
+// in use.  The chunked form keeps dU, the per-chunk state gradients, the per-chunk
+// dt_bias / A_log sums and (bf16) the reverse recurrence's operands; the token-level form
+// one partial sum per 16-column slice of V of dq, dk, dg, dbeta plus its per-token
+// operands and token-state scratch.
 BwdLayout bwd_layout(const Params &p, size_t fwd_bytes, bool chunked) {
     BwdLayout L{};
     const size_t Ttot = (size_t)p.B * p.T, f = sizeof(float);
@@ -316,19 +317,15 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes, bool chunked) {
     off = align256(off + f * ns * Ttot * p.HV * p.K);
     L.off_pdk = off;
     off = align256(off + f * ns * Ttot * p.HV * p.K);
-    L.off_pdg = off;
-    off = align256(off + f * ns * Ttot * p.HV * p.K);
-    L.off_pdb = off;
-    off = align256(off + f * ns * Ttot * p.HV);
-    L.off_da = off;
-    off = align256(off + f * Ttot * p.HV * p.K);
-    L.off_param = off;
-    off = align256(off + f * bwd_param_scratch_floats(p.HV, p.K));
     if (chunked) {
+        // dg and dbeta are final from the per-chunk kernel; dt_bias and A_log come from
+        // per-chunk sums
         L.off_du = off;
         off = align256(off + f * slots * p.C * p.V);
         L.off_dh = off;
         off = align256(off + f * slots * p.K * p.V);
+        L.off_cparam = off;
+        off = align256(off + f * slots * (p.K + 1));
         if (p.qkv_bf16) {  // the reverse recurrence's transposed operands and dO (bf16)
             L.off_rpack = off;
             off = align256(off + 2 * slots * 2 * p.C * p.K);
@@ -338,6 +335,14 @@ BwdLayout bwd_layout(const Params &p, size_t fwd_bytes, bool chunked) {
             off = align256(off + 2 * slots * p.V * p.C);
         }
     } else {
+        L.off_pdg = off;
+        off = align256(off + f * ns * Ttot * p.HV * p.K);
+        L.off_pdb = off;
+        off = align256(off + f * ns * Ttot * p.HV);
+        L.off_da = off;
+        off = align256(off + f * Ttot * p.HV * p.K);
+        L.off_param = off;
+        off = align256(off + f * bwd_param_scratch_floats(p.HV, p.K));
         const size_t scr = bwd_seq_scratch_floats(p.N, p.HV, p.K, p.V, p.C);
         L.off_sstate = off;
         off = align256(off + f * scr);
@@ -417,11 +422,11 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     b.nslices = L.nslices;
     b.p_dq = reinterpret_cast<float *>(ws + L.off_pdq);
     b.p_dk = reinterpret_cast<float *>(ws + L.off_pdk);
-    b.p_dg = reinterpret_cast<float *>(ws + L.off_pdg);
-    b.p_db = reinterpret_cast<float *>(ws + L.off_pdb);
-    b.scr_da = reinterpret_cast<float *>(ws + L.off_da);
-    b.scr_param = reinterpret_cast<float *>(ws + L.off_param);
     if (!chunked) {
+        b.p_dg = reinterpret_cast<float *>(ws + L.off_pdg);
+        b.p_db = reinterpret_cast<float *>(ws + L.off_pdb);
+        b.scr_da = reinterpret_cast<float *>(ws + L.off_da);
+        b.scr_param = reinterpret_cast<float *>(ws + L.off_param);
         b.scr_state = reinterpret_cast<float *>(ws + L.off_sstate);
         b.scr_w = reinterpret_cast<float *>(ws + L.off_sw);
         b.t_q = reinterpret_cast<float *>(ws + L.off_tq);
@@ -440,6 +445,7 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     P.b = b;
     P.dU = reinterpret_cast<float *>(ws + L.off_du);
     P.dh = reinterpret_cast<float *>(ws + L.off_dh);
+    P.cparam = reinterpret_cast<float *>(ws + L.off_cparam);
     if (p.qkv_bf16) {
         P.rpack = reinterpret_cast<uint16_t *>(ws + L.off_rpack);
         P.ppack = reinterpret_cast<uint16_t *>(ws + L.off_ppack);
@@ -447,7 +453,7 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     }
     hipError_t e = launch_bwd_dhu(P, stream);
     if (e == hipSuccess) e = launch_bwd_local(P, stream);
-    if (e == hipSuccess) e = launch_bwd_finish(b, stream);
+    if (e == hipSuccess) e = launch_bwd_finish_chunked(P, stream);
     return to_status(e);
 }
 

@@ -42,6 +42,7 @@ struct BwdChunkParams {
     uint16_t *rpack;                // Kg [C][K], W^T [K][C] (permuted row fragments)
     uint16_t *ppack;                // Aqk^T [C][C], Qg^T [K][C] (permuted row fragments)
     uint16_t *doq;                  // dO [V][C] in accumulator-tile order
+    float *cparam;                  // [total chunks * HV][K + 1] per-chunk dt_bias sums, then the A_log sum
 };
 
 // The chunked backward covers K <= 128 (the token-level form above that).
@@ -49,6 +50,7 @@ bool bwd_chunk_fits(int K);
 hipError_t launch_bwd_dhu(const BwdChunkParams &p, hipStream_t s);
 hipError_t launch_bwd_local(const BwdChunkParams &p, hipStream_t s);
 hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s);
+hipError_t launch_bwd_finish_chunked(const BwdChunkParams &p, hipStream_t s);
 
 int bwd_slices(int V);
 size_t bwd_seq_state_floats(int N, int HV, int K, int V, int C);

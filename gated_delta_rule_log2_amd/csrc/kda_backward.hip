@@ -310,39 +310,57 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
     }
 }
 
-// dq, dk per (token, qk head): the value heads of the group and the V slices summed,
-// then the scale and L2-norm chain rule.  Block of 256 threads, thread d < K.
+// dq, dk per (token, qk head): the value heads of the group and the partial sums
+// summed in order, then the scale and L2-norm chain rule.  One wave per (token, qk head)
+// row, four rows per block; lane l holds elements l, l + 64, ... of the row.
 __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
-    __shared__ float ws[4][4];
-    const int64_t t = blockIdx.x / p.H;
-    const int h = blockIdx.x % p.H, d = threadIdx.x;
-    const int group = p.HV / p.H, ns = p.nslices;
-    float gq = 0.f, gk = 0.f, qv = 0.f, kv = 0.f;
-    if (d < p.K) {
-        for (int jv = 0; jv < group; ++jv)
-            for (int sl = 0; sl < ns; ++sl) {
-                const size_t row = ((size_t)sl * p.Ttot + t) * p.HV + h * group + jv;
-                gq += p.p_dq[row * p.K + d];
-                gk += p.p_dk[row * p.K + d];
-            }
-        qv = ldf(p.q, (t * p.H + h) * p.K + d, p.qkv_bf16);
-        kv = ldf(p.k, (t * p.H + h) * p.K + d, p.qkv_bf16);
+    const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+    if (row >= p.Ttot * p.H) return;  // whole waves only; no block barrier below
+    const int64_t t = row / p.H;
+    const int h = (int)(row % p.H), l = threadIdx.x & 63;
+    const int group = p.HV / p.H, ns = p.nslices, K = p.K;
+    float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f},
+          kv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int d = l + 64 * e;
+        if (d < K) {
+            for (int jv = 0; jv < group; ++jv)
+                for (int sl = 0; sl < ns; ++sl) {
+                    const size_t r = ((size_t)sl * p.Ttot + t) * p.HV + h * group + jv;
+                    gq[e] += p.p_dq[r * K + d];
+                    gk[e] += p.p_dk[r * K + d];
+                }
+            qv[e] = ldf(p.q, row * K + d, p.qkv_bf16);
+            kv[e] = ldf(p.k, row * K + d, p.qkv_bf16);
+        }
     }
-    float dq = gq * p.scale, dk = gk;
+    float rq = 1.f, rk = 1.f, qd = 0.f, kd = 0.f;
     if (p.qk_l2norm) {
-        const float r0 = wave_sum(qv * qv), r1 = wave_sum(kv * kv), r2 = wave_sum(qv * gq), r3 = wave_sum(kv * gk);
-        if ((d & 63) == 0) ws[d >> 6][0] = r0, ws[d >> 6][1] = r1, ws[d >> 6][2] = r2, ws[d >> 6][3] = r3;
-        __syncthreads();
-        float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
-        for (int i = 0; i < kBwdThreads / 64; ++i) sq += ws[i][0], sk += ws[i][1], qd += ws[i][2], kd += ws[i][3];
-        const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
-        // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
-        dq = p.scale * (rq * gq - rq * rq * rq * qv * qd);
-        dk = rk * gk - rk * rk * rk * kv * kd;
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sq += qv[e] * qv[e];
+            sk += kv[e] * kv[e];
+            qd += qv[e] * gq[e];
+            kd += kv[e] * gk[e];
+        }
+        sq = wave_sum(sq), sk = wave_sum(sk), qd = wave_sum(qd), kd = wave_sum(kd);
+        rq = 1.f / sqrtf(sq + 1e-6f);
+        rk = 1.f / sqrtf(sk + 1e-6f);
     }
-    if (d < p.K) {
-        p.dq[(t * p.H + h) * p.K + d] = dq;
-        p.dk[(t * p.H + h) * p.K + d] = dk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int d = l + 64 * e;
+        if (d >= K) continue;
+        float dq = gq[e] * p.scale, dk = gk[e];
+        if (p.qk_l2norm) {
+            // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
+            dq = p.scale * (rq * gq[e] - rq * rq * rq * qv[e] * qd);
+            dk = rk * gk[e] - rk * rk * rk * kv[e] * kd;
+        }
+        p.dq[row * K + d] = dq;
+        p.dk[row * K + d] = dk;
     }
 }
 
@@ -468,13 +486,39 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
 // (activation chain rules), then the dt_bias and A_log token sums.
 hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s) {
     if (p.Ttot > 0) {
-        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)(p.Ttot * p.H)), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);
     }
     if (p.gate_mode != kGatePre) {
         hipLaunchKernelGGL(bwd_param_partial_kernel, dim3((unsigned)p.HV * kParamSegs), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, p);
     }
+    return hipGetLastError();
+}
+
+// dt_bias and A_log gradients of the chunked form: the per-chunk sums of every chunk of
+// the value head, added in chunk order.  One block per value head.
+__global__ void __launch_bounds__(kBwdThreads) bwd_chunk_param_kernel(BwdChunkParams P) {
+    const int hv = blockIdx.x, K = P.b.K, HV = P.b.HV, nc = P.f.total_chunks;
+    for (int d = threadIdx.x; d <= K; d += blockDim.x) {
+        float acc = 0.f;
+        for (int c = 0; c < nc; ++c) acc += P.cparam[((size_t)c * HV + hv) * (K + 1) + d];
+        if (d < K) {
+            if (P.b.ddt_bias) P.b.ddt_bias[(int64_t)hv * K + d] = acc;
+        } else if (P.b.dA_log) {
+            P.b.dA_log[hv] = acc;
+        }
+    }
+}
+
+// The chunked form's finishing kernels: dq and dk from the per-value-head partial sums
+// (dg and dbeta are final from the per-chunk kernel), then dt_bias and A_log.
+hipError_t launch_bwd_finish_chunked(const BwdChunkParams &P, hipStream_t s) {
+    const BwdParams &p = P.b;
+    if (p.Ttot > 0)
+        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
+    if (p.gate_mode != kGatePre && (p.ddt_bias || p.dA_log))
+        hipLaunchKernelGGL(bwd_chunk_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, P);
     return hipGetLastError();
 }
 

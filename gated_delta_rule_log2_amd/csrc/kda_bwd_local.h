@@ -191,20 +191,44 @@ struct LocalLds {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Four consecutive values of a row of q, k, g (storage bf16 or fp32) as fp32.
-__device__ __forceinline__ float4 load4_any(const void *base, int64_t idx, bool bf) {
-    if (bf) {
+// Four consecutive values as fp32 from storage type T (uint16_t: bf16; float).
+template <typename T>
+__device__ __forceinline__ float4 load4_t(const void *base, int64_t idx) {
+    if constexpr (sizeof(T) == 2) {
         const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
                            __uint_as_float(u.y & 0xffff0000u));
+    } else {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
     }
-    return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+}
+
+// The gate input and its bias for this lane's NT groups of four columns of one row:
+// every load issued before any is used (one dtype branch for the whole row).
+template <int NT>
+__device__ __forceinline__ void load_gate_row(const Params &p, int64_t grow, int hv, int cg, float4 (&gv)[NT],
+                                              float4 (&dbv)[NT]) {
+    if (p.g_bf16) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) gv[t] = load4_t<uint16_t>(p.g, grow + 16 * t + 4 * cg);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) gv[t] = load4_t<float>(p.g, grow + 16 * t + 4 * cg);
+    }
+    if (p.dt_bias && p.gate_mode != kGatePre) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            dbv[t] = *reinterpret_cast<const float4 *>(p.dt_bias + (int64_t)hv * p.K + 16 * t + 4 * cg);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dbv[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 template <int C, typename T, int NKK>
 __global__ void __launch_bounds__(C / 16 * 64) bwd_local_kernel(BwdChunkParams P) {
     constexpr int MP = sizeof(T) == 4 ? kMmaF32 : kMmaSplit;
-    constexpr int K = 32 * NKK, NB = C / 16, NT = K / 16, KH = K / 2, NTH = NT / 2;
+    constexpr int K = 32 * NKK, NB = C / 16, NT = K / 16, NTH = NT / 2;
     using L_ = LocalLds<C, K>;
     constexpr int LDM = L_::LDM, LDK = L_::LDK, LDV = L_::LDV, LDH = L_::LDH;
     const Params &p = P.f;
@@ -240,15 +264,17 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local_kernel(BwdChunkParams P
         const int64_t qrow = (tok * p.H + hq) * (int64_t)K, grow = (tok * p.HV + hv) * (int64_t)K;
         const float a = p.A_log ? expf(p.A_log[hv]) : 1.f;
         const float unit = valid ? kLog2e : 0.f;
+        float4 qv[NT], kv[NT], gv[NT], dbv[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int d0 = 16 * t + 4 * cg;
-            const float4 qv = load4_any(p.q, qrow + d0, p.qkv_bf16), kv = load4_any(p.k, qrow + d0, p.qkv_bf16);
-            const float4 gv = load4_any(p.g, grow + d0, p.g_bf16);
-            float4 db = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.dt_bias && p.gate_mode != kGatePre) db = *reinterpret_cast<const float4 *>(p.dt_bias + (int64_t)hv * K + d0);
-            const float qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
-            const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ba[4] = {db.x, db.y, db.z, db.w};
+            qv[t] = load4_t<T>(p.q, qrow + 16 * t + 4 * cg);
+            kv[t] = load4_t<T>(p.k, qrow + 16 * t + 4 * cg);
+        }
+        load_gate_row<NT>(p, grow, hv, cg, gv, dbv);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float qa[4] = {qv[t].x, qv[t].y, qv[t].z, qv[t].w}, ka[4] = {kv[t].x, kv[t].y, kv[t].z, kv[t].w};
+            const float ga[4] = {gv[t].x, gv[t].y, gv[t].z, gv[t].w}, ba[4] = {dbv[t].x, dbv[t].y, dbv[t].z, dbv[t].w};
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 qh[t][jj] = qa[jj];
@@ -481,23 +507,38 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local_kernel(BwdChunkParams P
         const float *dh = P.dh + slot * (size_t)K * V;
         const float *du = P.dU + slot * (size_t)C * V;
         for (int v0 = 0; v0 < V; v0 += 32) {
-            // stage (rows past the chunk's end as zeros)
-            for (int e = threadIdx.x; e < K * 8; e += blockDim.x) {
-                const int d = e >> 3, c4 = 4 * (e & 7);
-                *reinterpret_cast<float4 *>(SP + d * LDV + c4) = *reinterpret_cast<const float4 *>(hs + (size_t)d * V + v0 + c4);
-                *reinterpret_cast<float4 *>(DS + d * LDV + c4) = *reinterpret_cast<const float4 *>(dh + (size_t)d * V + v0 + c4);
+            // stage (rows past the chunk's end as zeros): every load of the block first
+            constexpr int NTHR = 64 * NB, NSD = K * 8 / NTHR, NCV = C * 8 / NTHR;
+            static_assert(K * 8 % NTHR == 0 && C * 8 % NTHR == 0, "staging split");
+            float4 sp4[NSD], ds4[NSD], do4[NCV], vv4[NCV], du4[NCV];
+#pragma unroll
+            for (int q = 0; q < NSD; ++q) {
+                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
+                sp4[q] = *reinterpret_cast<const float4 *>(hs + (size_t)d * V + v0 + c4);
+                ds4[q] = *reinterpret_cast<const float4 *>(dh + (size_t)d * V + v0 + c4);
             }
-            for (int e = threadIdx.x; e < C * 8; e += blockDim.x) {
-                const int r2 = e >> 3, c4 = 4 * (e & 7);
-                float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = o4;
-                if (r2 < ci.L) {
-                    const int64_t row = ((ci.tok0 + r2) * p.HV + hv) * (int64_t)V + v0 + c4;
-                    o4 = load4_any(bp.dout, row, bp.qkv_bf16);
-                    v4 = load4_any(p.v, row, p.qkv_bf16);
-                }
-                *reinterpret_cast<float4 *>(DO + r2 * LDV + c4) = o4;
-                *reinterpret_cast<float4 *>(VV + r2 * LDV + c4) = v4;
-                *reinterpret_cast<float4 *>(DU + r2 * LDV + c4) = *reinterpret_cast<const float4 *>(du + (size_t)r2 * V + v0 + c4);
+#pragma unroll
+            for (int q = 0; q < NCV; ++q) {
+                const int e = threadIdx.x + q * NTHR, r2 = e >> 3, c4 = 4 * (e & 7);
+                const int rr = r2 < ci.L ? r2 : ci.L - 1;  // in-bounds row, zeroed below
+                const int64_t row = ((ci.tok0 + rr) * p.HV + hv) * (int64_t)V + v0 + c4;
+                do4[q] = load4_t<T>(bp.dout, row);
+                vv4[q] = load4_t<T>(p.v, row);
+                du4[q] = *reinterpret_cast<const float4 *>(du + (size_t)r2 * V + v0 + c4);
+            }
+#pragma unroll
+            for (int q = 0; q < NSD; ++q) {
+                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
+                *reinterpret_cast<float4 *>(SP + d * LDV + c4) = sp4[q];
+                *reinterpret_cast<float4 *>(DS + d * LDV + c4) = ds4[q];
+            }
+#pragma unroll
+            for (int q = 0; q < NCV; ++q) {
+                const int e = threadIdx.x + q * NTHR, r2 = e >> 3, c4 = 4 * (e & 7);
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4 *>(DO + r2 * LDV + c4) = r2 < ci.L ? do4[q] : z;
+                *reinterpret_cast<float4 *>(VV + r2 * LDV + c4) = r2 < ci.L ? vv4[q] : z;
+                *reinterpret_cast<float4 *>(DU + r2 * LDV + c4) = du4[q];
             }
             __syncthreads();
             // Y = b v - X S_prev (lane: rows 16w + 4cg + jj, column 16vt + lr)
@@ -891,16 +932,65 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local_kernel(BwdChunkParams P
             for (int bb = w + 1; bb < NB; ++bb) suf += TOT[bb * K + 16 * t + 4 * cg + jj];
             dG[t][jj] += suf;
         }
+    // the gate's chain rule (dg w.r.t. the g given), this chunk's sums for dt_bias and
+    // A_log, and dbeta through the beta transform
+    const size_t o = (size_t)tok * p.HV + hv;
+    const float a_h = p.A_log ? expf(p.A_log[hv]) : 1.f;
+    float sda = 0.f;
+    {
+        float4 gv[NT], dbv[NT];
+        load_gate_row<NT>(p, (int64_t)o * K, hv, cg, gv, dbv);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float ga[4] = {gv[t].x, gv[t].y, gv[t].z, gv[t].w}, ba[4] = {dbv[t].x, dbv[t].y, dbv[t].z, dbv[t].w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float da;
+                dG[t][jj] = gate_act_grad(p.gate_mode, valid ? dG[t][jj] : 0.f, ga[jj], ba[jj], a_h, p.lower_bound, da);
+                sda += da;
+            }
+        }
+    }
     if (valid) {
-        const size_t o = (size_t)(ci.tok0 + i) * p.HV + hv;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int d0 = 16 * t + 4 * cg;
             *reinterpret_cast<float4 *>(bp.p_dq + o * K + d0) = make_float4(dqh[t][0], dqh[t][1], dqh[t][2], dqh[t][3]);
             *reinterpret_cast<float4 *>(bp.p_dk + o * K + d0) = make_float4(dkh[t][0], dkh[t][1], dkh[t][2], dkh[t][3]);
-            *reinterpret_cast<float4 *>(bp.p_dg + o * K + d0) = make_float4(dG[t][0], dG[t][1], dG[t][2], dG[t][3]);
+            *reinterpret_cast<float4 *>(bp.dg + o * K + d0) = make_float4(dG[t][0], dG[t][1], dG[t][2], dG[t][3]);
         }
-        if (cg == 0) bp.p_db[o] = DBETA[i] + db3;
+        if (cg == 0) {
+            float dbv = DBETA[i] + db3;
+            if (p.beta_mode != kBetaGiven) {
+                const float s = 1.f / (1.f + expf(-load_any(p.beta, (int64_t)o, p.beta_bf16)));
+                dbv *= (p.beta_mode == kBetaTwoSigmoid ? 2.f : 1.f) * s * (1.f - s);
+            }
+            bp.dbeta[o] = dbv;
+        }
+    }
+    if (p.gate_mode != kGatePre) {
+        // column sums over the chunk's rows (rows past the end hold dg = 0), then over waves
+        __syncthreads();  // TOT's suffix totals read
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float cs = row_sum16_all(dG[t][jj]);
+                if (lr == 0) TOT[w * K + 16 * t + 4 * cg + jj] = cs;
+            }
+        sda = sum_col_groups(row_sum16_all(sda));
+        if (l == 0) DGAM[w] = sda;
+        __syncthreads();
+        float *part = P.cparam + slot * (K + 1);
+        for (int d = threadIdx.x; d <= K; d += blockDim.x) {
+            float acc = 0.f;
+            if (d < K) {
+                for (int bb = 0; bb < NB; ++bb) acc += TOT[bb * K + d];
+            } else {
+                for (int bb = 0; bb < NB; ++bb) acc += DGAM[bb];
+            }
+            part[d] = acc;
+        }
     }
 }
 

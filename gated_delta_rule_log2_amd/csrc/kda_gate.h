@@ -69,6 +69,25 @@ __device__ __forceinline__ float gate_act(int mode, float graw, float dtb, float
     return (lb * unit) * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(a * kLog2e) * x));
 }
 
+// Chain rule of gate_act in natural-log units: from gp = dL/dg' returns dL/dg and sets
+// da to the element's term of dL/dA_log (a = exp(A_log[hv]); 0 when pre-gated).
+//   softplus:  dg'/dg = -a sigmoid(x),          dg'/dA_log = g' = -a softplus(x)
+//   bounded:   dg'/dg = lb a s (1 - s), s = sigmoid(a x),   dg'/dA_log = lb a x s (1 - s)
+__device__ __forceinline__ float gate_act_grad(int mode, float gp, float graw, float dtb, float a, float lb, float &da) {
+    da = 0.f;
+    if (mode == kGatePre) return gp;
+    const float x = graw + dtb;
+    if (mode == kGateSoftplus) {
+        const float sp = x > 20.f ? x : log1pf(expf(x));
+        da = gp * (-a * sp);
+        return gp * (-a) / (1.f + expf(-x));
+    }
+    const float s = 1.f / (1.f + expf(-a * x));
+    const float ds = lb * s * (1.f - s) * a;
+    da = gp * ds * x;
+    return gp * ds;
+}
+
 __device__ __forceinline__ float beta_act(int mode, float b) {
     if (mode == kBetaGiven) return b;
     const float s = 1.f / (1.f + expf(-b));

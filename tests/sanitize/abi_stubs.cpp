@@ -22,6 +22,7 @@ hipError_t launch_backward(const BwdParams &, hipStream_t) { ++g_stub_launches; 
 hipError_t launch_bwd_dhu(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_local(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_finish(const BwdParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+hipError_t launch_bwd_finish_chunked(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 bool bwd_chunk_fits(int K) { return K <= 128; }
 }  // namespace kda
 
