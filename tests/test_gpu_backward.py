@@ -34,11 +34,11 @@ CASES = [
 ]
 
 
-def gpu_grads(inp, kw, do, dht):
+def gpu_grads(inp, kw, do, dht, tokenwise=False):
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     out = chunk_kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.to(DEV),
                         dht=None if dht is None else dht.to(DEV), A_log=d["A_log"], dt_bias=d["dt_bias"],
-                        initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], **kw)
+                        initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], tokenwise=tokenwise, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -86,6 +86,49 @@ def test_backward_parity(w):
         e = rel_frobenius(x, r)
         print(f"{w.name} {key}: rel-Frobenius {e:.3e}", flush=True)
         assert e <= tol, f"{w.name} {key}: rel-Frobenius {e:.3e} > {tol}"
+
+
+CROSS = [w for w in CASES if w.name in ("bwd_tiny_fp32_h0", "bwd_gva_bf16", "bwd_varlen_c32_k96_v32",
+                                        "bwd_pregated_negeig")]
+
+
+@pytest.mark.parametrize("w", CROSS, ids=[w.name for w in CROSS])
+def test_chunked_matches_tokenwise(w):
+    """The chunked backward against the token-level form (kda_chunk_bwd_tokenwise, fp32
+    token steps from the same chunk-start states) on the GPU: 1e-4 for fp32 inputs
+    (both sides fp32 throughout); 2e-2 for bf16 inputs, where the chunked form's
+    operands are the forward's bf16 intermediates."""
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    kw = kernel_kwargs(w)
+    kw.pop("output_final_state", None)
+    do, dht = cotangents(inp)
+    got = gpu_grads(inp, kw, do, dht)
+    ref = gpu_grads(inp, kw, do, dht, tokenwise=True)
+    tol = 1e-4 if w.dtype == torch.float32 else 2e-2
+    for key in got:
+        e = rel_frobenius(to_np(got[key]), to_np(ref[key]))
+        print(f"{w.name} {key}: chunked vs token-level {e:.3e}", flush=True)
+        assert e <= tol, f"{w.name} {key}: chunked vs token-level {e:.3e} > {tol}"
+
+
+def test_chunked_matches_tokenwise_full_size():
+    """The metric configuration (B=1, T=8192, H=16, HV=32, K=V=128) in the benchmark's
+    launch configuration: every gradient of every head, chunked against the token-level
+    form."""
+    w = GVA_BF16
+    inp = make_inputs(w)
+    kw = kernel_kwargs(w)
+    kw.pop("output_final_state", None)
+    do, dht = cotangents(inp)
+    got = gpu_grads(inp, kw, do, dht)
+    ref = gpu_grads(inp, kw, do, dht, tokenwise=True)
+    for key in got:
+        x, r = got[key].float(), ref[key].float()
+        assert torch.isfinite(x).all(), f"{key}: non-finite"
+        e = (torch.linalg.vector_norm(x - r) / torch.linalg.vector_norm(r)).item()
+        print(f"full size {key}: chunked vs token-level {e:.3e}", flush=True)
+        assert e <= 2e-2, f"full size {key}: chunked vs token-level {e:.3e}"
 
 
 def test_backward_edges():
