@@ -312,55 +312,52 @@ __global__ void __launch_bounds__(kSeqThreads) bwd_seq_kernel(BwdParams p) {
 
 // dq, dk per (token, qk head): the value heads of the group and the partial sums
 // summed in order, then the scale and L2-norm chain rule.  One wave per (token, qk head)
-// row, four rows per block; lane l holds elements l, l + 64, ... of the row.
+// row, four rows per block; lane l holds elements 4l .. 4l + 3 of the row (K <= 256).
+__device__ __forceinline__ float4 ld4(const void *p, int64_t i, bool bf) {
+    if (bf) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                           __uint_as_float(u.y & 0xffff0000u));
+    }
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+}
+
 __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
     const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
     if (row >= p.Ttot * p.H) return;  // whole waves only; no block barrier below
     const int64_t t = row / p.H;
     const int h = (int)(row % p.H), l = threadIdx.x & 63;
     const int group = p.HV / p.H, ns = p.nslices, K = p.K;
-    float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f},
-          kv[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int d = l + 64 * e;
-        if (d < K) {
-            for (int jv = 0; jv < group; ++jv)
-                for (int sl = 0; sl < ns; ++sl) {
-                    const size_t r = ((size_t)sl * p.Ttot + t) * p.HV + h * group + jv;
-                    gq[e] += p.p_dq[r * K + d];
-                    gk[e] += p.p_dk[r * K + d];
-                }
-            qv[e] = ldf(p.q, row * K + d, p.qkv_bf16);
-            kv[e] = ldf(p.k, row * K + d, p.qkv_bf16);
-        }
+    const bool on = 4 * l < K;
+    float4 gq = make_float4(0.f, 0.f, 0.f, 0.f), gk = gq, qv = gq, kv = gq;
+    if (on) {
+        for (int sl = 0; sl < ns; ++sl)
+            for (int jv = 0; jv < group; ++jv) {
+                const size_t r = (((size_t)sl * p.Ttot + t) * p.HV + h * group + jv) * K + 4 * l;
+                const float4 a = *reinterpret_cast<const float4 *>(p.p_dq + r);
+                const float4 b = *reinterpret_cast<const float4 *>(p.p_dk + r);
+                gq.x += a.x, gq.y += a.y, gq.z += a.z, gq.w += a.w;
+                gk.x += b.x, gk.y += b.y, gk.z += b.z, gk.w += b.w;
+            }
+        qv = ld4(p.q, row * K + 4 * l, p.qkv_bf16);
+        kv = ld4(p.k, row * K + 4 * l, p.qkv_bf16);
     }
-    float rq = 1.f, rk = 1.f, qd = 0.f, kd = 0.f;
+    float4 dq = make_float4(gq.x * p.scale, gq.y * p.scale, gq.z * p.scale, gq.w * p.scale), dk = gk;
     if (p.qk_l2norm) {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sq += qv[e] * qv[e];
-            sk += kv[e] * kv[e];
-            qd += qv[e] * gq[e];
-            kd += kv[e] * gk[e];
-        }
-        sq = wave_sum(sq), sk = wave_sum(sk), qd = wave_sum(qd), kd = wave_sum(kd);
-        rq = 1.f / sqrtf(sq + 1e-6f);
-        rk = 1.f / sqrtf(sk + 1e-6f);
+        const float sq = wave_sum(qv.x * qv.x + qv.y * qv.y + qv.z * qv.z + qv.w * qv.w);
+        const float sk = wave_sum(kv.x * kv.x + kv.y * kv.y + kv.z * kv.z + kv.w * kv.w);
+        const float qd = wave_sum(qv.x * gq.x + qv.y * gq.y + qv.z * gq.z + qv.w * gq.w);
+        const float kd = wave_sum(kv.x * gk.x + kv.y * gk.y + kv.z * gk.z + kv.w * gk.w);
+        const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
+        // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
+        const float cq = rq * rq * rq * qd, ck = rk * rk * rk * kd;
+        dq = make_float4(p.scale * (rq * gq.x - cq * qv.x), p.scale * (rq * gq.y - cq * qv.y),
+                         p.scale * (rq * gq.z - cq * qv.z), p.scale * (rq * gq.w - cq * qv.w));
+        dk = make_float4(rk * gk.x - ck * kv.x, rk * gk.y - ck * kv.y, rk * gk.z - ck * kv.z, rk * gk.w - ck * kv.w);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int d = l + 64 * e;
-        if (d >= K) continue;
-        float dq = gq[e] * p.scale, dk = gk[e];
-        if (p.qk_l2norm) {
-            // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
-            dq = p.scale * (rq * gq[e] - rq * rq * rq * qv[e] * qd);
-            dk = rk * gk[e] - rk * rk * rk * kv[e] * kd;
-        }
-        p.dq[row * K + d] = dq;
-        p.dk[row * K + d] = dk;
+    if (on) {
+        *reinterpret_cast<float4 *>(p.dq + row * K + 4 * l) = dq;
+        *reinterpret_cast<float4 *>(p.dk + row * K + 4 * l) = dk;
     }
 }
 
@@ -497,12 +494,24 @@ hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s) {
 }
 
 // dt_bias and A_log gradients of the chunked form: the per-chunk sums of every chunk of
-// the value head, added in chunk order.  One block per value head.
-__global__ void __launch_bounds__(kBwdThreads) bwd_chunk_param_kernel(BwdChunkParams P) {
+// the value head.  One block of 1024 threads per value head: 8 stripes of 128 columns,
+// stripe j adding chunks j, j + 8, ... in order, then the 8 stripe sums in order, so the
+// result does not depend on scheduling.
+constexpr int kParamStripes = 8;
+
+__global__ void __launch_bounds__(1024) bwd_chunk_param_kernel(BwdChunkParams P) {
+    __shared__ float part[kParamStripes][257 + 1];
     const int hv = blockIdx.x, K = P.b.K, HV = P.b.HV, nc = P.f.total_chunks;
+    const int stripe = threadIdx.x >> 7, c0 = threadIdx.x & 127;
+    for (int d = c0; d <= K; d += 128) {
+        float acc = 0.f;
+        for (int c = stripe; c < nc; c += kParamStripes) acc += P.cparam[((size_t)c * HV + hv) * (K + 1) + d];
+        part[stripe][d] = acc;
+    }
+    __syncthreads();
     for (int d = threadIdx.x; d <= K; d += blockDim.x) {
         float acc = 0.f;
-        for (int c = 0; c < nc; ++c) acc += P.cparam[((size_t)c * HV + hv) * (K + 1) + d];
+        for (int j = 0; j < kParamStripes; ++j) acc += part[j][d];
         if (d < K) {
             if (P.b.ddt_bias) P.b.ddt_bias[(int64_t)hv * K + d] = acc;
         } else if (P.b.dA_log) {
@@ -518,7 +527,7 @@ hipError_t launch_bwd_finish_chunked(const BwdChunkParams &P, hipStream_t s) {
     if (p.Ttot > 0)
         hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
     if (p.gate_mode != kGatePre && (p.ddt_bias || p.dA_log))
-        hipLaunchKernelGGL(bwd_chunk_param_kernel, dim3((unsigned)p.HV), dim3(kBwdThreads), 0, s, P);
+        hipLaunchKernelGGL(bwd_chunk_param_kernel, dim3((unsigned)p.HV), dim3(1024), 0, s, P);
     return hipGetLastError();
 }
 
