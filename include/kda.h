@@ -228,7 +228,7 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
  *            (also without initial_state: the gradient at a zero initial state)
  * Workspace: kda_chunk_bwd_workspace_size bytes, device memory owned by the caller,
  * not retained (the forward's workspace, the chunk-start states, dU and the per-chunk
- * state gradients: 1.58 GB at B = 1, T = 8192, HV = 32, K = V = 128, bf16).  Errors: those of
+ * state gradients: 1.61 GB at B = 1, T = 8192, HV = 32, K = V = 128, bf16).  Errors: those of
  * kda_chunk_fwd, KDA_ERR_NULL_POINTER for a missing dout or required output when
  * B*T > 0.  Asynchronous on `stream`.  Results do not depend on scheduling (no atomics).
  */
