@@ -3,7 +3,8 @@
     python -m gated_delta_rule_log2_amd.build
 
 Every translation unit is compiled for gfx950 only, with packed-fp32 code
-generation turned off, into _build/, then linked next to this file.
+generation turned off, into _build/, then linked next to this file; the linked
+code is scanned for misplaced spill stores (codecheck.py) before it is installed.
 """
 from __future__ import annotations
 
@@ -51,6 +52,13 @@ def build_library(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # spill stores placed under a region's exec mask at a join (codecheck.py) give wrong
+    # reloads at run time; such a build is refused before it replaces the library
+    from . import codecheck
+    findings = codecheck.check_library(tmp)
+    if findings:
+        os.remove(tmp)
+        raise RuntimeError("spill stores under a narrowed exec mask in the built code:\n" + "\n".join(findings))
     os.replace(tmp, LIBRARY)
     if verbose:
         print(f"built {LIBRARY}")
