@@ -176,13 +176,14 @@ const char *kda_chunk_fwd_stage_name(int i) { return (i >= 0 && i < kNumStages) 
 }  // extern "C"
 
 // The whole forward: checks, then plan -> intra -> recurrence on `stream`.  `states`
-// (the state each chunk starts from) is written when want_states; `ev` as for
-// kda_chunk_fwd_profiled.
+// (the state each chunk starts from) is written when want_states, in the recurrence's
+// fragment order when states_frag (only where the register-resident recurrence runs);
+// `ev` as for kda_chunk_fwd_profiled.
 kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                             const int64_t *cu_seqlens, void *o, float *final_state, bool want_states,
                             float *states, void *workspace, size_t workspace_bytes, hipStream_t stream,
-                            hipEvent_t *ev) {
+                            hipEvent_t *ev, bool states_frag) {
     Params p;
     kda_status st = check_desc(d, p);
     if (st != KDA_OK) return st;
@@ -201,6 +202,7 @@ kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *
     p.cu_seqlens = cu_seqlens;
     p.o = o; p.ht = final_state;
     p.hs = want_states ? states : nullptr;
+    p.hs_frag = want_states && states_frag ? 1 : 0;
     bind_workspace(p, workspace, L);
 
     hipError_t (*const stages[kNumStages])(const Params &, hipStream_t) = {launch_plan, launch_intra,
@@ -403,7 +405,7 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     kda_fwd_desc fd = *d;
     fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
     st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
-                       states, workspace, FL.total_bytes, stream, nullptr);
+                       states, workspace, FL.total_bytes, stream, nullptr, chunked && p.qkv_bf16);
     if (st != KDA_OK) return st;
 
     BwdParams b{};

@@ -217,12 +217,12 @@ bwd_dhu_reg_kernel(BwdChunkParams P) {
             uint2 p1[NMT];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) p1[mt] = PB[(2 * mt + j) * 64 + l];
-            // the gradient of the state after this chunk, for the per-chunk gradients
-            float *gdh = P.dh + (sl * K + 4 * cg) * (size_t)V + col;
+            // the gradient of the state after this chunk, for the per-chunk gradients, in
+            // fragment order: float4 ((v0 / 32 * 2 + j) * NT + t) * 64 + lane of the chunk's
+            // K x V block holds rows 16t + 4cg .. +3 of column v0 + 16 j + lr
+            float4 *gdh = reinterpret_cast<float4 *>(P.dh + sl * K * (size_t)V) + ((size_t)(v0 / kBV) * 2 + j) * NT * 64 + l;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) gdh[(size_t)(16 * t + jj) * V] = dS[t][jj];
+            for (int t = 0; t < NT; ++t) gdh[t * 64] = make_float4(dS[t][0], dS[t][1], dS[t][2], dS[t][3]);
             uint4 Sb[NKK];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
@@ -249,11 +249,10 @@ bwd_dhu_reg_kernel(BwdChunkParams P) {
                 Ub[ms] = make_uint4(pack2(-dU[2 * ms][0], -dU[2 * ms][1]), pack2(-dU[2 * ms][2], -dU[2 * ms][3]),
                                     pack2(-dU[2 * ms + 1][0], -dU[2 * ms + 1][1]),
                                     pack2(-dU[2 * ms + 1][2], -dU[2 * ms + 1][3]));
-            float *gdu = P.dU + (sl * C + 4 * cg) * (size_t)V + col;
+            // dU in the same fragment order over the chunk's C x V block (NMT row tiles)
+            float4 *gdu = reinterpret_cast<float4 *>(P.dU + sl * C * (size_t)V) + ((size_t)(v0 / kBV) * 2 + j) * NMT * 64 + l;
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) gdu[(size_t)(16 * mt + jj) * V] = dU[mt][jj];
+            for (int mt = 0; mt < NMT; ++mt) gdu[mt * 64] = make_float4(dU[mt][0], dU[mt][1], dU[mt][2], dU[mt][3]);
             // dS <- Diag(d) dS + P2 - W^T dU
 #pragma unroll
             for (int t = 0; t < NT; ++t) {

@@ -92,6 +92,20 @@ __device__ __forceinline__ f32x4 mma16_ss(f32x4 acc, uint2 ah, uint2 al, uint2 b
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, ah), __builtin_bit_cast(s16x4, bh), acc, 0, 0, 0);
 }
 
+// The chunk-start state, the state gradient and dU arrive in the fragment order of the
+// recurrences that wrote them: within a (chunk, value head) block of R rows and V
+// columns, float4 index (vs * 2 + j) * (R / 16) * 64 + f' with f' = t * 64 + lane holds
+// rows 16t + 4cg .. +3 of one column of the 32-column slice vs.  frag_rows_col gives,
+// for the float4 index f within a slice, its first row and its column in the slice:
+// the forward recurrence's state waves hold column 8 (lr / 4) + 4 j + lr % 4 (HM =
+// false), the reverse recurrence's column 16 j + lr (HM = true).
+template <int R, bool HM>
+__device__ __forceinline__ void frag_rows_col(int f, int &row0, int &col) {
+    const int ln = f & 63, tj = f >> 6, t = tj % (R / 16), j = tj / (R / 16), lr = ln & 15;
+    row0 = 16 * t + 4 * (ln >> 4);
+    col = HM ? 16 * j + lr : 8 * (lr >> 2) + 4 * j + (lr & 3);
+}
+
 template <int C, int K>
 struct LocalLds2 {
     static constexpr int NB = C / 16, NPAIR = NB * (NB - 1) / 2, KH = K / 2;
@@ -476,11 +490,10 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
             // S_prev and v first (staged now); dS, dU, dO are loaded after Y
             float4 sp4[NSD];
             uint4 vv8[NC8];
+            const size_t fslice = (size_t)(v0 / 32) * (K * 8);  // float4s of one slice of a [K][V] block
 #pragma unroll
-            for (int q = 0; q < NSD; ++q) {
-                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
-                sp4[q] = *reinterpret_cast<const float4 *>(hs + (size_t)d * V + v0 + c4);
-            }
+            for (int q = 0; q < NSD; ++q)
+                sp4[q] = reinterpret_cast<const float4 *>(hs)[fslice + threadIdx.x + q * NTHR];
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
                 const int e = threadIdx.x + q * NTHR, r2 = e >> 2, c8 = 8 * (e & 3);
@@ -489,15 +502,16 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
                                                           ((ci.tok0 + rr) * p.HV + hv) * (int64_t)V + v0 + c8);
                 if (r2 >= ci.L) vv8[q] = make_uint4(0u, 0u, 0u, 0u);
             }
-            // (a) S_prev [d][v] and S_prev^T [v][d], v [i][v]
+            // (a) S_prev [d][v] and S_prev^T [v][d] (each float4: rows d0..d0+3 of column c), v [i][v]
 #pragma unroll
             for (int q = 0; q < NSD; ++q) {
-                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
-                split_store4(SPh, SPl, d * LB32 + c4, sp4[q].x, sp4[q].y, sp4[q].z, sp4[q].w);
-                split_store1(SPTh, SPTl, (c4 + 0) * LBK + d, sp4[q].x);
-                split_store1(SPTh, SPTl, (c4 + 1) * LBK + d, sp4[q].y);
-                split_store1(SPTh, SPTl, (c4 + 2) * LBK + d, sp4[q].z);
-                split_store1(SPTh, SPTl, (c4 + 3) * LBK + d, sp4[q].w);
+                int d0, c;
+                frag_rows_col<K, false>(threadIdx.x + q * NTHR, d0, c);
+                split_store4(SPTh, SPTl, c * LBK + d0, sp4[q].x, sp4[q].y, sp4[q].z, sp4[q].w);
+                split_store1(SPh, SPl, (d0 + 0) * LB32 + c, sp4[q].x);
+                split_store1(SPh, SPl, (d0 + 1) * LB32 + c, sp4[q].y);
+                split_store1(SPh, SPl, (d0 + 2) * LB32 + c, sp4[q].z);
+                split_store1(SPh, SPl, (d0 + 3) * LB32 + c, sp4[q].w);
             }
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
@@ -531,15 +545,10 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
             float4 ds4[NSD], du4[NCV];
             uint4 do8[NC8];
 #pragma unroll
-            for (int q = 0; q < NSD; ++q) {
-                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
-                ds4[q] = *reinterpret_cast<const float4 *>(dh + (size_t)d * V + v0 + c4);
-            }
+            for (int q = 0; q < NSD; ++q) ds4[q] = reinterpret_cast<const float4 *>(dh)[fslice + threadIdx.x + q * NTHR];
 #pragma unroll
-            for (int q = 0; q < NCV; ++q) {
-                const int e = threadIdx.x + q * NTHR, r2 = e >> 3, c4 = 4 * (e & 7);
-                du4[q] = *reinterpret_cast<const float4 *>(du + (size_t)r2 * V + v0 + c4);
-            }
+            for (int q = 0; q < NCV; ++q)
+                du4[q] = reinterpret_cast<const float4 *>(du)[(size_t)(v0 / 32) * (C * 8) + threadIdx.x + q * NTHR];
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
                 const int e = threadIdx.x + q * NTHR, r2 = e >> 2, c8 = 8 * (e & 3);
@@ -563,29 +572,22 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
             // (b) dS [d][v], dO, dU [i][v], dU^T [v][i]; rowsum(S_prev o dS) (S_prev as hi + lo)
 #pragma unroll
             for (int q = 0; q < NSD; ++q) {
-                const int e = threadIdx.x + q * NTHR, d = e >> 3, c4 = 4 * (e & 7);
-                split_store4(DSh, DSl, d * LB32 + c4, ds4[q].x, ds4[q].y, ds4[q].z, ds4[q].w);
-                const uint2 sh = *reinterpret_cast<const uint2 *>(SPh + d * LB32 + c4);
-                const uint2 sl = *reinterpret_cast<const uint2 *>(SPl + d * LB32 + c4);
-                const float s0 = __uint_as_float(sh.x << 16) + __uint_as_float(sl.x << 16);
-                const float s1 = __uint_as_float(sh.x & 0xffff0000u) + __uint_as_float(sl.x & 0xffff0000u);
-                const float s2 = __uint_as_float(sh.y << 16) + __uint_as_float(sl.y << 16);
-                const float s3 = __uint_as_float(sh.y & 0xffff0000u) + __uint_as_float(sl.y & 0xffff0000u);
-                // the 8 lanes of row d are consecutive: sum them into DD[d]
-                float sd = s0 * ds4[q].x + s1 * ds4[q].y + s2 * ds4[q].z + s3 * ds4[q].w;
-                sd += __shfl_xor(sd, 1, 64);
-                sd += __shfl_xor(sd, 2, 64);
-                sd += __shfl_xor(sd, 4, 64);
-                if ((e & 7) == 0) DD[d] += sd;
+                int d0, c;
+                frag_rows_col<K, true>(threadIdx.x + q * NTHR, d0, c);
+                split_store1(DSh, DSl, (d0 + 0) * LB32 + c, ds4[q].x);
+                split_store1(DSh, DSl, (d0 + 1) * LB32 + c, ds4[q].y);
+                split_store1(DSh, DSl, (d0 + 2) * LB32 + c, ds4[q].z);
+                split_store1(DSh, DSl, (d0 + 3) * LB32 + c, ds4[q].w);
             }
 #pragma unroll
             for (int q = 0; q < NCV; ++q) {
-                const int e = threadIdx.x + q * NTHR, r2 = e >> 3, c4 = 4 * (e & 7);
-                split_store4(DUh, DUl, r2 * LB32 + c4, du4[q].x, du4[q].y, du4[q].z, du4[q].w);
-                split_store1(DUTh, DUTl, (c4 + 0) * LBC + r2, du4[q].x);
-                split_store1(DUTh, DUTl, (c4 + 1) * LBC + r2, du4[q].y);
-                split_store1(DUTh, DUTl, (c4 + 2) * LBC + r2, du4[q].z);
-                split_store1(DUTh, DUTl, (c4 + 3) * LBC + r2, du4[q].w);
+                int r0, c;
+                frag_rows_col<C, true>(threadIdx.x + q * NTHR, r0, c);
+                split_store4(DUTh, DUTl, c * LBC + r0, du4[q].x, du4[q].y, du4[q].z, du4[q].w);
+                split_store1(DUh, DUl, (r0 + 0) * LB32 + c, du4[q].x);
+                split_store1(DUh, DUl, (r0 + 1) * LB32 + c, du4[q].y);
+                split_store1(DUh, DUl, (r0 + 2) * LB32 + c, du4[q].z);
+                split_store1(DUh, DUl, (r0 + 3) * LB32 + c, du4[q].w);
             }
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
@@ -593,6 +595,26 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
                 *reinterpret_cast<uint4 *>(DOp + r2 * LB32 + c8) = do8[q];
             }
             __syncthreads();
+            // rowsum(S_prev o dS) of this block into DD (both as hi + lo), TPR threads per row
+            {
+                constexpr int TPR = NTHR / K >= 8 ? 8 : (NTHR / K >= 4 ? 4 : (NTHR / K >= 2 ? 2 : 1));
+                constexpr int CPT = 32 / TPR;
+                const int dr = (int)threadIdx.x / TPR, d = dr < K ? dr : K - 1, c0 = CPT * ((int)threadIdx.x % TPR);
+                auto lo16 = [](uint32_t x) { return __uint_as_float(x << 16); };
+                auto hi16 = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+                float sd = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPT; c += 4) {
+                    const int a = d * LB32 + c0 + c;
+                    const uint2 sh = *reinterpret_cast<const uint2 *>(SPh + a), sl = *reinterpret_cast<const uint2 *>(SPl + a);
+                    const uint2 gh = *reinterpret_cast<const uint2 *>(DSh + a), gl = *reinterpret_cast<const uint2 *>(DSl + a);
+                    sd += (lo16(sh.x) + lo16(sl.x)) * (lo16(gh.x) + lo16(gl.x)) + (hi16(sh.x) + hi16(sl.x)) * (hi16(gh.x) + hi16(gl.x)) +
+                          (lo16(sh.y) + lo16(sl.y)) * (lo16(gh.y) + lo16(gl.y)) + (hi16(sh.y) + hi16(sl.y)) * (hi16(gh.y) + hi16(gl.y));
+                }
+#pragma unroll
+                for (int m = 1; m < TPR; m <<= 1) sd += __shfl_xor(sd, m, 64);
+                if ((int)threadIdx.x % TPR == 0 && dr < K) DD[d] += sd;
+            }
             // this wave's rows i = 16w + lr as the second operand (contraction over v)
             const int ri = (16 * w + lr) * LB32 + 8 * cg;
             const uint4 bO = *reinterpret_cast<const uint4 *>(DOp + ri);

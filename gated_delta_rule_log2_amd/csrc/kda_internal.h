@@ -32,6 +32,8 @@ struct Params {
     void *o;
     float *ht;
     float *hs;                     // [total_chunks, HV, K, V] state each chunk starts from, or nullptr
+    int32_t hs_frag;               // hs in the register-resident recurrence's fragment order
+                                   // (backward hand-over; see recur_reg_kernel), else [K][V] / [V][K]
     float *g_act, *g_cum;          // gate-only entry point
     // workspace
     int32_t *chunk_off;            // [N + 1] first global chunk of each sequence
@@ -69,5 +71,6 @@ namespace kda {
 kda_status chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                          const int64_t *cu_seqlens, void *o, float *final_state, bool want_states, float *states,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev,
+                         bool states_frag = false);
 }  // namespace kda

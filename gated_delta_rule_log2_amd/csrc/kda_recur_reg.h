@@ -119,7 +119,12 @@ __device__ __forceinline__ void ring_issue_k(const Params &p, unsigned char *rin
 }
 
 // HS: also write the state each chunk starts from (p.hs); a separate instantiation so
-// the stores add no register pressure to the plain forward.
+// the stores add no register pressure to the plain forward.  With p.hs_frag the states
+// are written in this kernel's own fragment order, one 16-byte store per lane and tile:
+// within the K x V state of a (chunk, value head), the float4 at index
+// ((vs * 2 + j) * NT + t) * 64 + lane holds rows 16t + 4cg .. +3 of column
+// 32 vs + 8 (lr / 4) + 4 j + lr % 4 (vs: 32-column slice, j: state wave, lane = 16 cg + lr)
+// -- the backward's per-chunk kernel reads that order back.
 template <int C, int NKK, bool HS>
 __global__ void __launch_bounds__(64 * (4 + C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 recur_reg_kernel(Params p) {
@@ -174,7 +179,11 @@ recur_reg_kernel(Params p) {
         const uint32_t hs_lane = p.state_vk ? (uint32_t)col * K + 4 * cg : (uint32_t)(4 * cg) * V + col;
         auto put_states = [&](int k) {
             float *hb = p.hs + ((size_t)(c0 + k) * p.HV + hv) * K * V;
-            if (p.state_vk) {
+            if (p.hs_frag) {
+                float4 *fb = reinterpret_cast<float4 *>(hb) + ((size_t)(v0 / kBV) * 2 + j) * NT * 64 + l;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) fb[t * 64] = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+            } else if (p.state_vk) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)  // rows 16t + 4cg .. +3 are contiguous in [V][K]
                     *reinterpret_cast<float4 *>(hb + hs_lane + 16 * t) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
