@@ -124,7 +124,7 @@ __device__ __forceinline__ void ring_issue_k(const Params &p, unsigned char *rin
 // within the K x V state of a (chunk, value head), the float4 at index
 // ((vs * 2 + j) * NT + t) * 64 + lane holds rows 16t + 4cg .. +3 of column
 // 32 vs + 8 (lr / 4) + 4 j + lr % 4 (vs: 32-column slice, j: state wave, lane = 16 cg + lr)
-// -- the backward's per-chunk kernel reads that order back.
+// -- the backward's per-chunk kernel reads that order back; that pass computes no output.
 template <int C, int NKK, bool HS>
 __global__ void __launch_bounds__(64 * (4 + C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 recur_reg_kernel(Params p) {
@@ -317,6 +317,15 @@ recur_reg_kernel(Params p) {
         }
     } else if (!is_loader) {
         // ------------------------------------------------------------ output wave o
+        if constexpr (HS) {
+            if (p.hs_frag) {
+                // the backward's recompute needs the states, not the output: these waves
+                // only take part in the barriers (the prologue's and one per step, as below)
+                __syncthreads();
+                for (int m = 0; m <= nsteps; ++m) __syncthreads();
+                return;
+            }
+        }
         const int o = out_idx;
         const int mt0 = o;
         // this wave's rows of Qg [NKK] and of the non-zero Aqk blocks [NMS]
