@@ -82,7 +82,8 @@ __device__ __forceinline__ float gate_act_grad(int mode, float gp, float graw, f
         da = gp * (-a * sp);
         return gp * (-a) / (1.f + expf(-x));
     }
-    const float s = 1.f / (1.f + expf(-a * x));
+    // s as gate_act evaluates it: 1 / (1 + 2^(-a log2(e) x)), 0 once the power overflows
+    const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(a * kLog2e) * x));
     const float ds = lb * s * (1.f - s) * a;
     da = gp * ds * x;
     return gp * ds;
