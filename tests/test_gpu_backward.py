@@ -31,6 +31,10 @@ CASES = [
     VARLEN_BF16.replace(name="bwd_varlen_c32_k96_v32", num_seqs=3, min_len=20, max_len=90, H=1, HV=3, K=96, V=32,
                         chunk=32),
     TINY_FP32.replace(name="bwd_fp32_gva3_k32", T=77, H=1, HV=3, K=32, V=96, h0="normal0.1"),
+    # the two-wave per-chunk kernel at chunk 32, and the one-wave form at K = 32
+    VARLEN_BF16.replace(name="bwd_varlen_c32_k128", num_seqs=3, min_len=10, max_len=80, H=1, HV=2, K=128, V=64,
+                        chunk=32),
+    GVA_BF16.replace(name="bwd_gva_bf16_k32", T=90, H=1, HV=2, K=32, V=64),
 ]
 
 
