@@ -222,7 +222,9 @@ bwd_dhu_reg_kernel(BwdChunkParams P) {
             // K x V block holds rows 16t + 4cg .. +3 of column v0 + 16 j + lr
             float4 *gdh = reinterpret_cast<float4 *>(P.dh + sl * K * (size_t)V) + ((size_t)(v0 / kBV) * 2 + j) * NT * 64 + l;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) gdh[t * 64] = make_float4(dS[t][0], dS[t][1], dS[t][2], dS[t][3]);
+            for (int t = 0; t < NT; ++t)  // read back by a later kernel: non-temporal
+                store16_once(gdh + t * 64, make_uint4(__float_as_uint(dS[t][0]), __float_as_uint(dS[t][1]),
+                                                      __float_as_uint(dS[t][2]), __float_as_uint(dS[t][3])));
             uint4 Sb[NKK];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
@@ -252,7 +254,9 @@ bwd_dhu_reg_kernel(BwdChunkParams P) {
             // dU in the same fragment order over the chunk's C x V block (NMT row tiles)
             float4 *gdu = reinterpret_cast<float4 *>(P.dU + sl * C * (size_t)V) + ((size_t)(v0 / kBV) * 2 + j) * NMT * 64 + l;
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) gdu[mt * 64] = make_float4(dU[mt][0], dU[mt][1], dU[mt][2], dU[mt][3]);
+            for (int mt = 0; mt < NMT; ++mt)
+                store16_once(gdu + mt * 64, make_uint4(__float_as_uint(dU[mt][0]), __float_as_uint(dU[mt][1]),
+                                                       __float_as_uint(dU[mt][2]), __float_as_uint(dU[mt][3])));
             // dS <- Diag(d) dS + P2 - W^T dU
 #pragma unroll
             for (int t = 0; t < NT; ++t) {

@@ -182,7 +182,9 @@ recur_reg_kernel(Params p) {
             if (p.hs_frag) {
                 float4 *fb = reinterpret_cast<float4 *>(hb) + ((size_t)(v0 / kBV) * 2 + j) * NT * 64 + l;
 #pragma unroll
-                for (int t = 0; t < NT; ++t) fb[t * 64] = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+                for (int t = 0; t < NT; ++t)  // read back by a later kernel: non-temporal
+                    store16_once(fb + t * 64, make_uint4(__float_as_uint(S[t][0]), __float_as_uint(S[t][1]),
+                                                         __float_as_uint(S[t][2]), __float_as_uint(S[t][3])));
             } else if (p.state_vk) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)  // rows 16t + 4cg .. +3 are contiguous in [V][K]
