@@ -25,6 +25,17 @@
 
 namespace kda {
 
+// Streams read or written exactly once here (the chunk-start states, the state gradients,
+// dU; the per-value-head dq^, dk^, dg, dv): non-temporal, so they do not displace the
+// operands the workgroups share through the caches.
+__device__ __forceinline__ float4 load4_once(const float *p) {
+    const uint4 u = load16_once(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ void store4_once(float *p, float4 v) {
+    store16_once(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+
 template <int C, int K>
 struct LocalLds3 {
     static constexpr int NB = C / 16, NPAIR = NB * (NB - 1) / 2, KH = K / 2;
@@ -452,7 +463,7 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
             const size_t fslice = (size_t)(v0 / 32) * (K * 8);
             float4 sp4[NSD];
 #pragma unroll
-            for (int q = 0; q < NSD; ++q) sp4[q] = reinterpret_cast<const float4 *>(hs)[fslice + threadIdx.x + q * NTHR];
+            for (int q = 0; q < NSD; ++q) sp4[q] = load4_once(hs + 4 * (fslice + threadIdx.x + q * NTHR));
             uint4 vv8 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.v) +
                                                          ((ci.tok0 + rr8) * p.HV + hv) * (int64_t)V + v0 + c8);
             if (r8 >= ci.L) vv8 = make_uint4(0u, 0u, 0u, 0u);
@@ -491,10 +502,10 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
             // dS, dU, dO: in flight while Y and V_new are formed
             float4 ds4[NSD], du4[NCV];
 #pragma unroll
-            for (int q = 0; q < NSD; ++q) ds4[q] = reinterpret_cast<const float4 *>(dh)[fslice + threadIdx.x + q * NTHR];
+            for (int q = 0; q < NSD; ++q) ds4[q] = load4_once(dh + 4 * (fslice + threadIdx.x + q * NTHR));
 #pragma unroll
             for (int q = 0; q < NCV; ++q)
-                du4[q] = reinterpret_cast<const float4 *>(du)[(size_t)(v0 / 32) * (C * 8) + threadIdx.x + q * NTHR];
+                du4[q] = load4_once(du + 4 * ((size_t)(v0 / 32) * (C * 8) + threadIdx.x + q * NTHR));
             uint4 do8 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(bp.dout) +
                                                          ((ci.tok0 + rr8) * p.HV + hv) * (int64_t)V + v0 + c8);
             if (r8 >= ci.L) do8 = make_uint4(0u, 0u, 0u, 0u);
@@ -606,8 +617,8 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
                 dbv_acc += __uint_as_float(vq.x << 16) * acc[0] + __uint_as_float(vq.x & 0xffff0000u) * acc[1] +
                            __uint_as_float(vq.y << 16) * acc[2] + __uint_as_float(vq.y & 0xffff0000u) * acc[3];
                 if (valid)
-                    *reinterpret_cast<float4 *>(bp.dv + ((ci.tok0 + i) * p.HV + hv) * (int64_t)V + v0 + 16 * vt + 4 * cg) =
-                        make_float4(b_i * acc[0], b_i * acc[1], b_i * acc[2], b_i * acc[3]);
+                    store4_once(bp.dv + ((ci.tok0 + i) * p.HV + hv) * (int64_t)V + v0 + 16 * vt + 4 * cg,
+                                make_float4(b_i * acc[0], b_i * acc[1], b_i * acc[2], b_i * acc[3]));
             }
             __syncthreads();  // the next block's staging overwrites these buffers
         }
@@ -998,9 +1009,9 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
 #pragma unroll
         for (int u = 0; u < NTO; ++u) {
             const int d0 = 16 * tof(u) + 4 * cg;
-            *reinterpret_cast<float4 *>(bp.p_dq + o * K + d0) = make_float4(dqh[u][0], dqh[u][1], dqh[u][2], dqh[u][3]);
-            *reinterpret_cast<float4 *>(bp.p_dk + o * K + d0) = make_float4(dkh[u][0], dkh[u][1], dkh[u][2], dkh[u][3]);
-            *reinterpret_cast<float4 *>(bp.dg + o * K + d0) = make_float4(dG[u][0], dG[u][1], dG[u][2], dG[u][3]);
+            store4_once(bp.p_dq + o * K + d0, make_float4(dqh[u][0], dqh[u][1], dqh[u][2], dqh[u][3]));
+            store4_once(bp.p_dk + o * K + d0, make_float4(dkh[u][0], dkh[u][1], dkh[u][2], dkh[u][3]));
+            store4_once(bp.dg + o * K + d0, make_float4(dG[u][0], dG[u][1], dG[u][2], dG[u][3]));
         }
         // (every DB term was added before the barriers above)
         if (h == 0 && cg == 0) {
