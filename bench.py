@@ -306,6 +306,11 @@ def bench_bwd(args, w, inp, d, desc, args_, stream, lib, hip):
 
     ms = timed(lib.kda_chunk_bwd, bargs, args.steps, min(args.warmup, 2))
     ms_fwd = timed(lib.kda_chunk_fwd, args_, 20, 5)
+    # recomputation switched off: the saving forward, then the backward from what it kept
+    # (the backward only reads the saved part, so repeated calls time the same work)
+    sargs = args_[:11] + (p(ws), ws.numel(), stream)
+    ms_fwd_save = timed(lib.kda_chunk_fwd_save, sargs, 20, 2)
+    ms_saved = timed(lib.kda_chunk_bwd_saved, bargs, args.steps, min(args.warmup, 2))
     ntok = B * T
     eb = d["q"].element_size()
     # read: the forward's inputs, do and dht; written: the fp32 gradients
@@ -323,6 +328,9 @@ def bench_bwd(args, w, inp, d, desc, args_, stream, lib, hip):
                      "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "whole call",
                      "kernel_ms": round(ms, 4)},
         "path": {"algorithmic_bytes": alg_bytes, "forward_ms": round(ms_fwd, 5)},
+        "disable_recompute": {"forward_save_ms": round(ms_fwd_save, 5), "backward_saved_ms": round(ms_saved, 4),
+                              "what": "kda_chunk_fwd_save keeps the per-chunk intermediates and chunk-start "
+                                      "states; kda_chunk_bwd_saved starts from them (no forward recompute)"},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -158,6 +158,26 @@ def workspace_bytes(q, v, g, beta, *, chunk_size=64, cu_seqlens=None, scale=None
     return n.value
 
 
+class KDASaved:
+    """The forward's per-chunk intermediates and chunk-start states, kept by chunk_kda with
+    disable_recompute for one chunk_kda_bwd(..., saved=...) call (the backward then skips
+    recomputing them).  `workspace` is the device buffer that holds them (sized by
+    kda_chunk_bwd_workspace_size); `key` identifies the call they belong to.  The backward
+    only reads them, so one KDASaved serves any number of backward calls."""
+
+    def __init__(self, workspace: torch.Tensor, key: tuple):
+        self.workspace = workspace
+        self.key = key
+
+
+def _saved_key(desc, *tensors) -> tuple:
+    d = desc.d
+    cu = None if desc.cu_host is None else tuple(int(x) for x in desc.cu_host)
+    fields = (d.B, d.T, d.H, d.HV, d.K, d.V, d.chunk_size, d.num_seqs, d.qkv_dtype, d.g_dtype, d.beta_dtype,
+              d.scale, d.lower_bound, d.flags & ~_abi.OUTPUT_FINAL_STATE)
+    return fields, cu, tuple(None if t is None else (t.data_ptr(), t.device.index) for t in tensors)
+
+
 def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
               output_final_state: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
@@ -169,7 +189,10 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               cp_context=None, state_v_first: bool = False, transpose_state_layout: bool = False,
               return_intermediate_states: bool = False, disable_recompute: bool = False):
     """KDA forward on the current HIP stream.  Returns (o, final_state or None), or
-    (o, final_state or None, h) with return_intermediate_states.
+    (o, final_state or None, h) with return_intermediate_states, or (o, final_state or
+    None, saved) with disable_recompute: saved (a KDASaved) holds the per-chunk
+    intermediates and chunk-start states for chunk_kda_bwd(..., saved=saved), which then
+    skips recomputing the forward (kda_chunk_fwd_save / kda_chunk_bwd_saved).
 
     q, k [B, T, H, K]; v [B, T, HV, V]; g [B, T, HV, K]; beta [B, T, HV];
     initial_state / final_state [N, HV, K, V] float32 (N = B, or len(cu_seqlens) - 1),
@@ -178,8 +201,12 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     or [1, total chunks, HV, K, V] with cu_seqlens (chunks restart at every sequence start),
     in the same state layout.  scale defaults to K ** -0.5.  The o dtype is the q/k/v dtype.
     """
-    _unsupported(cp_context=cp_context is not None, disable_recompute=disable_recompute)
+    _unsupported(cp_context=cp_context is not None)
     transpose = bool(state_v_first or transpose_state_layout)
+    if disable_recompute and (return_intermediate_states or transpose):
+        raise KDAContractError(_abi.STATUS["KDA_ERR_UNSUPPORTED"],
+                               "disable_recompute keeps [K, V] states for the backward: it does not combine "
+                               "with return_intermediate_states or a transposed state layout")
     lib = library()
     if q.dim() != 4 or v.dim() != 4:
         raise KDAContractError(_abi.STATUS["KDA_ERR_SHAPE"], "q, k, v must be 4-D [B, T, heads, dim]")
@@ -208,14 +235,26 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if cu_seqlens is not None:
         cu_dev = cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
     nbytes = ctypes.c_size_t(0)
-    rc = lib.kda_chunk_fwd_workspace_size(ctypes.byref(desc.d), ctypes.byref(nbytes))
+    size_fn = lib.kda_chunk_bwd_workspace_size if disable_recompute else lib.kda_chunk_fwd_workspace_size
+    rc = size_fn(ctypes.byref(desc.d), ctypes.byref(nbytes))
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    if workspace is None:
+    if disable_recompute:  # the caller's, or one of its own: handed back with the result
+        if workspace is None:
+            workspace = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
+    elif workspace is None:
         workspace = _workspace(dev, stream, nbytes.value)
     o = torch.empty((B, T, HV, V), dtype=q.dtype, device=dev)
     ht = torch.empty((N, HV) + sshape, dtype=torch.float32, device=dev) if output_final_state else None
+    if disable_recompute:
+        rc = lib.kda_chunk_fwd_save(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
+                                    _ptr(ht), _ptr(workspace), workspace.numel(), stream)
+        if rc != _abi.KDA_OK:
+            _raise(rc, lib)
+        key = _saved_key(desc, q, k, v, g, beta, A_log, dt_bias, initial_state)
+        return o, ht, KDASaved(workspace, key)
     if not return_intermediate_states:
         rc = lib.kda_chunk_fwd(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(o),
@@ -245,7 +284,8 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   lower_bound: Optional[float] = None, A_log: Optional[torch.Tensor] = None,
                   dt_bias: Optional[torch.Tensor] = None, use_beta_sigmoid_in_kernel: bool = False,
                   allow_neg_eigval: bool = False, *, workspace: Optional[torch.Tensor] = None,
-                  tokenwise: bool = False) -> dict:
+                  tokenwise: bool = False, disable_recompute: bool = False,
+                  saved: Optional[KDASaved] = None) -> dict:
     """Gradients of <do, o> + <dht, final_state> for chunk_kda's inputs, on the current
     HIP stream (the forward is recomputed inside).  Arguments as chunk_kda; do has o's
     shape and dtype, dht the final state's ([N, HV, K, V] float32) or None.  Returns
@@ -255,7 +295,17 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     chunked one.  The workspace is allocated per call from torch's caching allocator
     (stream-ordered, so it is reused once the call's work is done) unless one is given;
     the forward's cached workspace is never grown by a backward call.
+    saved: what chunk_kda(..., disable_recompute=True) returned for these same inputs;
+    the forward is then not recomputed (kda_chunk_bwd_saved, the same gradients bit for
+    bit) and saved's buffer serves as the workspace (the saved part is only read).
+    disable_recompute=True requires it.
     """
+    if disable_recompute and saved is None:
+        raise KDAContractError(_abi.STATUS["KDA_ERR_NULL_POINTER"],
+                               "disable_recompute needs saved= (chunk_kda(..., disable_recompute=True))")
+    if saved is not None:
+        if tokenwise:
+            raise KDAContractError(_abi.STATUS["KDA_ERR_UNSUPPORTED"], "saved serves the chunked backward only")
     lib = library()
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
@@ -277,13 +327,19 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     _check_tensor(initial_state, "initial_state", (N, HV, K, V), dev, torch.float32)
     _check_tensor(dht, "dht", (N, HV, K, V), dev, torch.float32)
     cu_dev = None if cu_seqlens is None else cu_seqlens.to(device=dev, dtype=torch.int64).contiguous()
+    if saved is not None:
+        if saved.key != _saved_key(desc, q, k, v, g, beta, A_log, dt_bias, initial_state):
+            raise KDAContractError(_abi.STATUS["KDA_ERR_WORKSPACE"],
+                                   "saved belongs to a forward call with other inputs or settings")
     nbytes = ctypes.c_size_t(0)
     size_fn = lib.kda_chunk_bwd_tokenwise_workspace_size if tokenwise else lib.kda_chunk_bwd_workspace_size
     rc = size_fn(ctypes.byref(desc.d), ctypes.byref(nbytes))
     if rc != _abi.KDA_OK:
         _raise(rc, lib)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    if workspace is None:
+    if saved is not None:
+        workspace = saved.workspace
+    elif workspace is None:
         workspace = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
@@ -293,7 +349,8 @@ def chunk_kda_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         out["dA_log"] = torch.empty((HV,), **f32)
     if dt_bias is not None:
         out["ddt_bias"] = torch.empty((HV * K,), **f32)
-    run = lib.kda_chunk_bwd_tokenwise if tokenwise else lib.kda_chunk_bwd
+    run = lib.kda_chunk_bwd_tokenwise if tokenwise else (lib.kda_chunk_bwd_saved if saved is not None
+                                                         else lib.kda_chunk_bwd)
     rc = run(ctypes.byref(desc.d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
                            _ptr(dt_bias), _ptr(initial_state), _ptr(cu_dev), _ptr(do), _ptr(dht),
                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),

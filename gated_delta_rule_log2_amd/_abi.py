@@ -34,7 +34,8 @@ EXPORTS = (
     "kda_gate_chunk_cumsum_workspace_size", "kda_gate_chunk_cumsum", "kda_chunk_fwd_stage_count",
     "kda_chunk_fwd_stage_name", "kda_chunk_fwd_profiled", "kda_fused_recurrent_fwd", "kda_chunk_fwd_states",
     "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
-    "kda_chunk_bwd_tokenwise_workspace_size", "kda_chunk_bwd_tokenwise",
+    "kda_chunk_bwd_tokenwise_workspace_size", "kda_chunk_bwd_tokenwise", "kda_chunk_fwd_save",
+    "kda_chunk_bwd_saved",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
@@ -103,6 +104,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_bwd_tokenwise_workspace_size.argtypes = [dp, szp]
     lib.kda_chunk_bwd_tokenwise.restype = ctypes.c_int
     lib.kda_chunk_bwd_tokenwise.argtypes = [dp] + [_vp] * 20 + [ctypes.c_size_t, _vp]
+    lib.kda_chunk_fwd_save.restype = ctypes.c_int
+    lib.kda_chunk_fwd_save.argtypes = [dp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    lib.kda_chunk_bwd_saved.restype = ctypes.c_int
+    lib.kda_chunk_bwd_saved.argtypes = [dp] + [_vp] * 20 + [ctypes.c_size_t, _vp]
     lib.kda_gate_chunk_cumsum.restype = ctypes.c_int
     lib.kda_gate_chunk_cumsum.argtypes = [dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     if path == LIBRARY:

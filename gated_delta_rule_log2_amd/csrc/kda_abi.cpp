@@ -183,7 +183,7 @@ kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *
                             const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                             const int64_t *cu_seqlens, void *o, float *final_state, bool want_states,
                             float *states, void *workspace, size_t workspace_bytes, hipStream_t stream,
-                            hipEvent_t *ev, bool states_frag) {
+                            hipEvent_t *ev, bool states_frag, bool skip_output) {
     Params p;
     kda_status st = check_desc(d, p);
     if (st != KDA_OK) return st;
@@ -203,6 +203,7 @@ kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *
     p.o = o; p.ht = final_state;
     p.hs = want_states ? states : nullptr;
     p.hs_frag = want_states && states_frag ? 1 : 0;
+    p.skip_output = want_states && skip_output ? 1 : 0;
     bind_workspace(p, workspace, L);
 
     hipError_t (*const stages[kNumStages])(const Params &, hipStream_t) = {launch_plan, launch_intra,
@@ -383,7 +384,7 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
                    const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                    const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk, float *dv,
                    float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0, void *workspace,
-                   size_t workspace_bytes, hipStream_t stream, bool tokenwise) {
+                   size_t workspace_bytes, hipStream_t stream, bool tokenwise, bool saved) {
     Params p;
     kda_status st = bwd_check(d, p);
     if (st != KDA_OK) return st;
@@ -401,12 +402,15 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     float *states = reinterpret_cast<float *>(ws + L.off_states);
 
     // backward steps 1-2: the forward with the state each chunk starts from (its output o
-    // is not needed); its per-chunk intermediates stay in the workspace
-    kda_fwd_desc fd = *d;
-    fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
-    st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr, true,
-                       states, workspace, FL.total_bytes, stream, nullptr, chunked && p.qkv_bf16);
-    if (st != KDA_OK) return st;
+    // is not needed); its per-chunk intermediates stay in the workspace.  `saved`: a
+    // kda_chunk_fwd_save call left them there already.
+    if (!saved) {
+        kda_fwd_desc fd = *d;
+        fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
+        st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr,
+                           true, states, workspace, FL.total_bytes, stream, nullptr, chunked && p.qkv_bf16, true);
+        if (st != KDA_OK) return st;
+    }
 
     BwdParams b{};
     b.N = p.N; b.T = p.T; b.H = p.H; b.HV = p.HV; b.K = p.K; b.V = p.V; b.C = p.C;
@@ -465,13 +469,40 @@ extern "C" {
 
 kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes) { return bwd_workspace(d, bytes, false); }
 
+kda_status kda_chunk_fwd_save(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
+                              const int64_t *cu_seqlens, void *o, float *final_state, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    Params p;
+    kda_status st = bwd_check(d, p);
+    if (st != KDA_OK) return st;
+    const bool chunked = bwd_chunk_fits(p.K);
+    const WorkspaceLayout FL = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4);
+    const BwdLayout L = bwd_layout(p, FL.total_bytes, chunked);
+    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    // the states and intermediates exactly as kda_chunk_bwd's recompute leaves them, and o
+    float *states = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + L.off_states);
+    return chunk_fwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, o, final_state, true, states,
+                         workspace, FL.total_bytes, stream, nullptr, chunked && p.qkv_bf16, false);
+}
+
+kda_status kda_chunk_bwd_saved(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, const float *A_log, const float *dt_bias,
+                               const float *initial_state, const int64_t *cu_seqlens, const void *dout,
+                               const float *dht, float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                               float *dA_log, float *ddt_bias, float *dh0, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    return bwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta,
+                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, false, true);
+}
+
 kda_status kda_chunk_bwd(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                          const int64_t *cu_seqlens, const void *dout, const float *dht, float *dq, float *dk,
                          float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias, float *dh0,
                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return bwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta,
-                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, false);
+                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, false, false);
 }
 
 kda_status kda_chunk_bwd_tokenwise_workspace_size(const kda_fwd_desc *d, size_t *bytes) {
@@ -485,7 +516,7 @@ kda_status kda_chunk_bwd_tokenwise(const kda_fwd_desc *d, const void *q, const v
                                    float *dA_log, float *ddt_bias, float *dh0, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
     return bwd_run(d, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dout, dht, dq, dk, dv, dg, dbeta,
-                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, true);
+                   dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, true, false);
 }
 
 }  // extern "C"

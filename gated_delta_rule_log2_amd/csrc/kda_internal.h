@@ -34,6 +34,8 @@ struct Params {
     float *hs;                     // [total_chunks, HV, K, V] state each chunk starts from, or nullptr
     int32_t hs_frag;               // hs in the register-resident recurrence's fragment order
                                    // (backward hand-over; see recur_reg_kernel), else [K][V] / [V][K]
+    int32_t skip_output;           // with hs: o is not needed (the backward's recompute), the
+                                   // register-resident recurrence leaves it unwritten
     float *g_act, *g_cum;          // gate-only entry point
     // workspace
     int32_t *chunk_off;            // [N + 1] first global chunk of each sequence
@@ -72,5 +74,5 @@ kda_status chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *k, co
                          const void *beta, const float *A_log, const float *dt_bias, const float *initial_state,
                          const int64_t *cu_seqlens, void *o, float *final_state, bool want_states, float *states,
                          void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev,
-                         bool states_frag = false);
+                         bool states_frag = false, bool skip_output = false);
 }  // namespace kda

@@ -124,7 +124,9 @@ __device__ __forceinline__ void ring_issue_k(const Params &p, unsigned char *rin
 // within the K x V state of a (chunk, value head), the float4 at index
 // ((vs * 2 + j) * NT + t) * 64 + lane holds rows 16t + 4cg .. +3 of column
 // 32 vs + 8 (lr / 4) + 4 j + lr % 4 (vs: 32-column slice, j: state wave, lane = 16 cg + lr)
-// -- the backward's per-chunk kernel reads that order back; that pass computes no output.
+// -- the backward's per-chunk kernel reads that order back.  With p.skip_output (the
+// backward's recompute, which needs the states and not o) the output waves only keep
+// the barrier count.
 template <int C, int NKK, bool HS>
 __global__ void __launch_bounds__(64 * (4 + C / 16)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 recur_reg_kernel(Params p) {
@@ -320,7 +322,7 @@ recur_reg_kernel(Params p) {
     } else if (!is_loader) {
         // ------------------------------------------------------------ output wave o
         if constexpr (HS) {
-            if (p.hs_frag) {
+            if (p.skip_output) {
                 // the backward's recompute needs the states, not the output: these waves
                 // only take part in the barriers (the prologue's and one per step, as below)
                 __syncthreads();

@@ -243,6 +243,46 @@ kda_status kda_chunk_bwd(const kda_fwd_desc *d,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The forward and backward with recomputation switched off (the disable_recompute
+ * switch of chunk_kda and of its backward, "flash-linear-attention KDA 内核工程实践…"
+ * §2.2 parameter list; "Reading Notes: Implementation Notes for KDA in FLA", backward
+ * signature): the forward keeps more of its intermediates in memory so that the backward
+ * need not rebuild them, trading memory for the time of backward steps 1-2.
+ *
+ * kda_chunk_fwd_save computes o and final_state exactly as kda_chunk_fwd does and, in
+ * `workspace`, leaves what kda_chunk_bwd's recompute would put there: the per-chunk
+ * intermediates (W, U, Kg, Qg, Aqk, the chunk decay) and the state each chunk starts
+ * from.  Arguments as kda_chunk_fwd, but the workspace must hold
+ * kda_chunk_bwd_workspace_size bytes (1.61 GB at B = 1, T = 8192, HV = 32, K = V = 128,
+ * bf16) and KDA_TRANSPOSE_STATE is refused (KDA_ERR_UNSUPPORTED), as for the backward.
+ *
+ * kda_chunk_bwd_saved returns the same gradients as kda_chunk_bwd, bit for bit, from a
+ * workspace that the last kda_chunk_fwd_save call on it filled for the same descriptor
+ * and the same q, k, v, g, beta, A_log, dt_bias, initial_state and cu_seqlens; it skips
+ * backward steps 1-2.  Arguments and errors as kda_chunk_bwd.  The library cannot check
+ * that the workspace matches: with another workspace the gradients are undefined (no
+ * fault: every access stays inside the workspace size that is checked).  Between the
+ * calls the caller keeps the workspace (it is owned by the caller and not retained); the
+ * backward only reads the saved part and uses the rest as scratch, so one
+ * kda_chunk_fwd_save serves any number of kda_chunk_bwd_saved calls (other dout, dht)
+ * issued one after another on one stream.  Both asynchronous on `stream`.
+ */
+kda_status kda_chunk_fwd_save(const kda_fwd_desc *d,
+                              const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *A_log, const float *dt_bias,
+                              const float *initial_state, const int64_t *cu_seqlens,
+                              void *o, float *final_state,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+kda_status kda_chunk_bwd_saved(const kda_fwd_desc *d,
+                               const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, const float *A_log, const float *dt_bias,
+                               const float *initial_state, const int64_t *cu_seqlens,
+                               const void *dout, const float *dht,
+                               float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                               float *dA_log, float *ddt_bias, float *dh0,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The same gradients as kda_chunk_bwd by the token-level form: after the forward with
  * chunk-start states, one workgroup per (sequence, value head, 16-column slice of V)
  * takes the token recurrence's reverse steps from the last token to the first.  Every

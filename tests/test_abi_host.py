@@ -176,10 +176,26 @@ def test_python_shim_rejects_unsupported_keywords():
     from gated_delta_rule_log2_amd import KDAContractError, chunk_kda
 
     x = torch.zeros(1, 4, 1, 32)
-    for kw in (dict(cp_context=object()), dict(disable_recompute=True)):
+    for kw in (dict(cp_context=object()), dict(disable_recompute=True, return_intermediate_states=True),
+               dict(disable_recompute=True, state_v_first=True)):
         with pytest.raises(KDAContractError):
             chunk_kda(x, x, x, x, x[..., 0], **kw)
     assert issubclass(KDAContractError, ValueError)
+
+
+def test_python_shim_saved_backward_contract():
+    """chunk_kda_bwd: disable_recompute without saved, and saved with the token-level
+    form, are refused before anything reaches the library."""
+    import torch
+
+    from gated_delta_rule_log2_amd import KDAContractError, KDASaved, chunk_kda_bwd
+
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(KDAContractError, match="needs saved"):
+        chunk_kda_bwd(x, x, x, x, x[..., 0], x, disable_recompute=True)
+    with pytest.raises(KDAContractError, match="chunked backward only"):
+        chunk_kda_bwd(x, x, x, x, x[..., 0], x, saved=KDASaved(torch.zeros(256, dtype=torch.uint8), ("x",)),
+                      tokenwise=True)
 
 
 def test_transposed_state_flag_and_states_entry_checks(lib):
@@ -221,3 +237,44 @@ def test_backward_entry_checks(lib):
     assert bwd_status(lib, desc(), ws=None) == S["KDA_ERR_WORKSPACE"]
     lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n))
     assert bwd_status(lib, desc(), ws_bytes=n.value - 1) == S["KDA_ERR_WORKSPACE"]
+
+
+def test_saved_forward_and_backward_entry_checks(lib):
+    """kda_chunk_fwd_save needs the backward's workspace size and refuses the transposed
+    state layout; kda_chunk_bwd_saved makes kda_chunk_bwd's checks; all before anything is
+    enqueued."""
+    n = ctypes.c_size_t(0)
+    lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n))
+    fwd_need = ws_status(lib, desc())[1]
+
+    def save(d, ws_bytes, **ptrs):
+        names = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "h0", "cu", "o", "ht", "ws"]
+        p = {nm: FAKE for nm in names}
+        p.update(dt_bias=None, h0=None, cu=None, ht=None)
+        p.update(ptrs)
+        return lib.kda_chunk_fwd_save(ctypes.byref(d), *[p[nm] for nm in names], ws_bytes, None)
+
+    assert save(desc(), fwd_need) == S["KDA_ERR_WORKSPACE"]  # the forward's size is not enough
+    assert save(desc(), n.value - 1) == S["KDA_ERR_WORKSPACE"]
+    assert save(desc(), n.value, ws=None) == S["KDA_ERR_WORKSPACE"]
+    assert save(desc(flags=_abi.TRANSPOSE_STATE), n.value) == S["KDA_ERR_UNSUPPORTED"]
+    assert save(desc(chunk_size=48), n.value) == S["KDA_ERR_CHUNK_SIZE"]
+    assert save(desc(), n.value, o=None) == S["KDA_ERR_NULL_POINTER"]
+    assert save(desc(flags=_abi.OUTPUT_FINAL_STATE), n.value) == S["KDA_ERR_NULL_POINTER"]
+    assert lib.kda_chunk_fwd_save(None, *([None] * 12), 0, None) == S["KDA_ERR_NULL_POINTER"]
+
+    def bwd_saved(d, **ptrs):
+        names = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "h0", "cu", "do", "dht", "dq", "dk", "dv", "dg",
+                 "dbeta", "dA_log", "ddt_bias", "dh0", "ws"]
+        ws_bytes = ptrs.pop("ws_bytes", 1 << 40)
+        p = {nm: FAKE for nm in names}
+        p.update(dt_bias=None, h0=None, cu=None, dht=None, dA_log=None, ddt_bias=None, dh0=None)
+        p.update(ptrs)
+        return lib.kda_chunk_bwd_saved(ctypes.byref(d), *[p[nm] for nm in names], ws_bytes, None)
+
+    assert bwd_saved(desc(flags=_abi.TRANSPOSE_STATE)) == S["KDA_ERR_UNSUPPORTED"]
+    assert bwd_saved(desc(H=3, HV=4)) == S["KDA_ERR_GVA"]
+    for missing in ("do", "dq", "dk", "dv", "dg", "dbeta", "q"):
+        assert bwd_saved(desc(), **{missing: None}) == S["KDA_ERR_NULL_POINTER"], missing
+    assert bwd_saved(desc(), ws=None) == S["KDA_ERR_WORKSPACE"]
+    assert bwd_saved(desc(), ws_bytes=n.value - 1) == S["KDA_ERR_WORKSPACE"]

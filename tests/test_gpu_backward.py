@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_log2_amd import chunk_kda_bwd
+from gated_delta_rule_log2_amd import KDAContractError, chunk_kda, chunk_kda_bwd
 from gated_delta_rule_log2_amd.workloads import (GVA_BF16, LONG_BF16, TINY_FP32, TRAINING_BF16, VARLEN_BF16, kernel_kwargs,
                                                 make_inputs)
 from oracle.kda_oracle_bwd import oracle_bwd
@@ -198,3 +198,51 @@ def test_backward_full_size_sampled_heads():
         e = rel_frobenius(xn, ref[key].reshape(xn.shape))
         print(f"gva_bf16 full size, heads 6-7, {key}: rel-Frobenius {e:.3e}", flush=True)
         assert e <= 2e-2, f"{key}: rel-Frobenius {e:.3e} > 2e-2"
+
+
+SAVED = [w for w in CASES if w.name in ("bwd_tiny_fp32_h0", "bwd_gva_bf16", "bwd_varlen_bf16", "bwd_k256_bf16",
+                                        "bwd_varlen_c32_k128")]
+
+
+def saved_roundtrip(w):
+    """chunk_kda with disable_recompute (kda_chunk_fwd_save) gives o and the final state of
+    the plain forward bit for bit; chunk_kda_bwd with its saved intermediates
+    (kda_chunk_bwd_saved) gives the recomputing backward's gradients bit for bit, also on
+    a second call from the same saved buffer; saved from other inputs is refused."""
+    inp = make_inputs(w)
+    kw = kernel_kwargs(w)
+    kw.pop("output_final_state", None)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    common = dict(A_log=d["A_log"], dt_bias=d["dt_bias"], initial_state=d["initial_state"],
+                  cu_seqlens=d["cu_seqlens"], **kw)
+    o, ht = chunk_kda(*args, output_final_state=True, **common)
+    o2, ht2, saved = chunk_kda(*args, output_final_state=True, disable_recompute=True, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(ht2, ht), f"{w.name}: the saving forward changed o / final_state"
+    do, dht = cotangents(inp)
+    do, dht = do.to(DEV), dht.to(DEV)
+    ref = chunk_kda_bwd(*args, do, dht=dht, **common)
+    with pytest.raises(KDAContractError, match="other inputs"):
+        chunk_kda_bwd(d["q"].clone(), *args[1:], do, dht=dht, saved=saved, **common)
+    got = chunk_kda_bwd(*args, do, dht=dht, saved=saved, **common)
+    torch.cuda.synchronize()
+    for key in ref:
+        assert torch.equal(got[key], ref[key]), f"{w.name} {key}: saved backward differs from the recomputing one"
+    again = chunk_kda_bwd(*args, do, dht=dht, saved=saved, **common)
+    torch.cuda.synchronize()
+    for key in ref:
+        assert torch.equal(again[key], ref[key]), f"{w.name} {key}: second backward from one saved buffer differs"
+    print(f"{w.name}: saved forward / backward bit-identical", flush=True)
+
+
+@pytest.mark.parametrize("w", SAVED, ids=[w.name for w in SAVED])
+def test_saved_forward_backward_bitwise(w):
+    print(f"case {w.name}", flush=True)
+    saved_roundtrip(w)
+
+
+def test_saved_forward_backward_bitwise_full_size():
+    """The same at the metric configuration (B=1, T=8192, H=16, HV=32, K=V=128)."""
+    print("case gva_bf16 full size", flush=True)
+    saved_roundtrip(GVA_BF16)
