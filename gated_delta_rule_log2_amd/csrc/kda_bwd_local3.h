@@ -428,15 +428,22 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
             }
             __syncthreads();
         }
-        // A and A^T as split planes (C * C is a multiple of the thread count)
+        // A and A^T as split planes: one 4 x 4 block per thread of the first C^2 / 16
+        // threads (whole waves, so the branch is uniform per wave), its four rows written
+        // to both planes with 8-byte stores
         constexpr int LBC = L_::LBC;
-        static_assert(C * C % NTHR == 0, "whole rounds");
+        static_assert(C * C / 16 <= NTHR && C * C / 16 % 64 == 0, "whole waves, one block each");
+        if (wid * 64 < C * C / 16) {
+            const int bt = (int)threadIdx.x, r0 = 4 * (bt / (C / 4)), c0 = 4 * (bt % (C / 4));
+            float4 a[4];
 #pragma unroll
-        for (int rnd = 0; rnd < C * C / NTHR; ++rnd) {
-            const int e = (int)threadIdx.x + rnd * NTHR, r2 = e / C, c2 = e % C;
-            const float x = AI[r2 * LDM + c2];
-            split_store1(AIh, AIl, r2 * LBC + c2, x);
-            split_store1(ATh, ATl, c2 * LBC + r2, x);
+            for (int rr = 0; rr < 4; ++rr) a[rr] = *reinterpret_cast<const float4 *>(AI + (r0 + rr) * LDM + c0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) split_store4(AIh, AIl, (r0 + rr) * LBC + c0, a[rr].x, a[rr].y, a[rr].z, a[rr].w);
+            split_store4(ATh, ATl, (c0 + 0) * LBC + r0, a[0].x, a[1].x, a[2].x, a[3].x);
+            split_store4(ATh, ATl, (c0 + 1) * LBC + r0, a[0].y, a[1].y, a[2].y, a[3].y);
+            split_store4(ATh, ATl, (c0 + 2) * LBC + r0, a[0].z, a[1].z, a[2].z, a[3].z);
+            split_store4(ATh, ATl, (c0 + 3) * LBC + r0, a[0].w, a[1].w, a[2].w, a[3].w);
         }
     }
     __syncthreads();
@@ -818,6 +825,9 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
     uint16_t *D2Th = reinterpret_cast<uint16_t *>(smc + L_::bD2Th), *D2Tl = reinterpret_cast<uint16_t *>(smc + L_::bD2Tl);
     // D1 = dAqk (lower, with the diagonal), D2 = dM (strictly lower), [i][j] and [j][i]:
     // column blocks s = 2 sl + h of this row block
+    // (the [i][j] planes after a quad transpose: lane qd then holds row 16w + 4cg + qd,
+    // columns 16s + lr - qd .. +3)
+    const int qd = lane_id() & 3;
 #pragma unroll
     for (int sl = 0; sl < NBO; ++sl) {
         const int s = 2 * sl + h;
@@ -827,9 +837,12 @@ __global__ void __launch_bounds__(C / 16 * 128) bwd_local3_kernel(BwdChunkParams
             const int r2 = 16 * w + 4 * cg + jj, c2 = 16 * s + lr;
             d1[jj] = (s <= w && c2 <= r2) ? dAq[sl][jj] : 0.f;
             d2[jj] = (s <= w) ? dMt[sl][jj] : 0.f;
-            split_store1(D1h, D1l, r2 * LBC + c2, d1[jj]);
-            split_store1(D2h, D2l, r2 * LBC + c2, d2[jj]);
         }
+        const int ot = (16 * w + 4 * cg + qd) * LBC + 16 * s + lr - qd;
+        const float4 t1 = quad_transpose(make_float4(d1[0], d1[1], d1[2], d1[3]));
+        const float4 t2 = quad_transpose(make_float4(d2[0], d2[1], d2[2], d2[3]));
+        split_store4(D1h, D1l, ot, t1.x, t1.y, t1.z, t1.w);
+        split_store4(D2h, D2l, ot, t2.x, t2.y, t2.z, t2.w);
         split_store4(D1Th, D1Tl, (16 * s + lr) * LBC + 16 * w + 4 * cg, d1[0], d1[1], d1[2], d1[3]);
         split_store4(D2Th, D2Tl, (16 * s + lr) * LBC + 16 * w + 4 * cg, d2[0], d2[1], d2[2], d2[3]);
     }
