@@ -106,6 +106,28 @@ __device__ __forceinline__ void frag_rows_col(int f, int &row0, int &col) {
     col = HM ? 16 * j + lr : 8 * (lr >> 2) + 4 * j + (lr & 3);
 }
 
+// 4 x 4 transpose inside each quad of lanes (lanes 4a .. 4a + 3): lane 4a + q returns, as
+// its element i, element q of lane 4a + i.  Two exchange rounds (partner lane q ^ 1, then
+// q ^ 2), each moving the two elements whose index bit differs from the lane's bit.  The
+// recurrences hand over four consecutive rows of one column per lane, and the four lanes
+// of a quad hold four consecutive columns; after the transpose each lane holds four
+// consecutive columns of one row, so a [row][column] plane takes one 8-byte store per lane
+// and plane instead of four 2-byte ones.
+__device__ __forceinline__ float4 quad_transpose(float4 x) {
+    const int q = lane_id() & 3;
+    const bool q0 = (q & 1) != 0, q1 = (q & 2) != 0;
+    auto xor1 = [](float v) {  // quad_perm [1, 0, 3, 2]
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
+    };
+    auto xor2 = [](float v) {  // quad_perm [2, 3, 0, 1]
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
+    };
+    const float r0 = xor1(q0 ? x.x : x.y), r1 = xor1(q0 ? x.z : x.w);
+    const float t0 = q0 ? r0 : x.x, t1 = q0 ? x.y : r0, t2 = q0 ? r1 : x.z, t3 = q0 ? x.w : r1;
+    const float v0 = xor2(q1 ? t0 : t2), v1 = xor2(q1 ? t1 : t3);
+    return make_float4(q1 ? v0 : t0, q1 ? v1 : t1, q1 ? t2 : v0, q1 ? t3 : v1);
+}
+
 template <int C, int K>
 struct LocalLds2 {
     static constexpr int NB = C / 16, NPAIR = NB * (NB - 1) / 2, KH = K / 2;
@@ -486,6 +508,9 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
         static_assert(K * 8 % NTHR == 0 && C * 8 % NTHR == 0 && C * 4 % NTHR == 0, "staging split");
         const int njm = (16 * w + 16 + 31) / 32;  // 32-blocks of j <= 16w + 15
         const int jm0 = (16 * w) / 32;           // first 32-block of j >= 16w
+        // the four lanes of a quad hold four consecutive columns (c - qd .. c - qd + 3) of
+        // the same four rows in every fragment-order unit they load (frag_rows_col)
+        const int qd = lane_id() & 3;
         for (int v0 = 0; v0 < V; v0 += 32) {
             // S_prev and v first (staged now); dS, dU, dO are loaded after Y
             float4 sp4[NSD];
@@ -508,10 +533,8 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
                 int d0, c;
                 frag_rows_col<K, false>(threadIdx.x + q * NTHR, d0, c);
                 split_store4(SPTh, SPTl, c * LBK + d0, sp4[q].x, sp4[q].y, sp4[q].z, sp4[q].w);
-                split_store1(SPh, SPl, (d0 + 0) * LB32 + c, sp4[q].x);
-                split_store1(SPh, SPl, (d0 + 1) * LB32 + c, sp4[q].y);
-                split_store1(SPh, SPl, (d0 + 2) * LB32 + c, sp4[q].z);
-                split_store1(SPh, SPl, (d0 + 3) * LB32 + c, sp4[q].w);
+                const float4 tq = quad_transpose(sp4[q]);  // row d0 + qd, columns c - qd ..
+                split_store4(SPh, SPl, (d0 + qd) * LB32 + c - qd, tq.x, tq.y, tq.z, tq.w);
             }
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
@@ -574,20 +597,16 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_local2_kernel(BwdChunkParams 
             for (int q = 0; q < NSD; ++q) {
                 int d0, c;
                 frag_rows_col<K, true>(threadIdx.x + q * NTHR, d0, c);
-                split_store1(DSh, DSl, (d0 + 0) * LB32 + c, ds4[q].x);
-                split_store1(DSh, DSl, (d0 + 1) * LB32 + c, ds4[q].y);
-                split_store1(DSh, DSl, (d0 + 2) * LB32 + c, ds4[q].z);
-                split_store1(DSh, DSl, (d0 + 3) * LB32 + c, ds4[q].w);
+                const float4 tq = quad_transpose(ds4[q]);  // row d0 + qd, columns c - qd ..
+                split_store4(DSh, DSl, (d0 + qd) * LB32 + c - qd, tq.x, tq.y, tq.z, tq.w);
             }
 #pragma unroll
             for (int q = 0; q < NCV; ++q) {
                 int r0, c;
                 frag_rows_col<C, true>(threadIdx.x + q * NTHR, r0, c);
                 split_store4(DUTh, DUTl, c * LBC + r0, du4[q].x, du4[q].y, du4[q].z, du4[q].w);
-                split_store1(DUh, DUl, (r0 + 0) * LB32 + c, du4[q].x);
-                split_store1(DUh, DUl, (r0 + 1) * LB32 + c, du4[q].y);
-                split_store1(DUh, DUl, (r0 + 2) * LB32 + c, du4[q].z);
-                split_store1(DUh, DUl, (r0 + 3) * LB32 + c, du4[q].w);
+                const float4 tq = quad_transpose(du4[q]);
+                split_store4(DUh, DUl, (r0 + qd) * LB32 + c - qd, tq.x, tq.y, tq.z, tq.w);
             }
 #pragma unroll
             for (int q = 0; q < NC8; ++q) {
