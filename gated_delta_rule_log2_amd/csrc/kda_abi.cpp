@@ -11,6 +11,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_backward.h"
@@ -175,6 +176,19 @@ const char *kda_chunk_fwd_stage_name(int i) { return (i >= 0 && i < kNumStages) 
 
 }  // extern "C"
 
+// The forward's pointer checks (inputs, outputs, A_log, cu_seqlens against the descriptor).
+static kda_status fwd_pointer_checks(const kda_fwd_desc *d, const void *q, const void *k, const void *v, const void *g,
+                                     const void *beta, const float *A_log, const int64_t *cu_seqlens, const void *o,
+                                     const float *final_state) {
+    const bool tokens = (int64_t)d->B * d->T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_OUTPUT_FINAL_STATE) && !final_state) return KDA_ERR_NULL_POINTER;
+    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
+        return KDA_ERR_MISSING_A_LOG;
+    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    return KDA_OK;
+}
+
 // The whole forward: checks, then plan -> intra -> recurrence on `stream`.  `states`
 // (the state each chunk starts from) is written when want_states, in the recurrence's
 // fragment order when states_frag (only where the register-resident recurrence runs);
@@ -188,12 +202,8 @@ kda_status kda::chunk_fwd_run(const kda_fwd_desc *d, const void *q, const void *
     kda_status st = check_desc(d, p);
     if (st != KDA_OK) return st;
     if (want_states && p.total_chunks > 0 && !states) return KDA_ERR_NULL_POINTER;
-    const bool tokens = (int64_t)d->B * d->T > 0;
-    if (tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
-    if ((d->flags & KDA_OUTPUT_FINAL_STATE) && !final_state) return KDA_ERR_NULL_POINTER;
-    if ((d->flags & KDA_GATE_IN_KERNEL) && !(d->flags & KDA_HAS_LOWER_BOUND) && !A_log)
-        return KDA_ERR_MISSING_A_LOG;
-    if ((cu_seqlens == nullptr) != (d->cu_seqlens_host == nullptr)) return KDA_ERR_VARLEN;
+    st = fwd_pointer_checks(d, q, k, v, g, beta, A_log, cu_seqlens, o, final_state);
+    if (st != KDA_OK) return st;
     const WorkspaceLayout L = workspace_layout(p.N, p.total_chunks, p.HV, p.K, p.V, p.C, p.qkv_bf16 ? 2 : 4);
     if (!workspace || workspace_bytes < L.total_bytes) return KDA_ERR_WORKSPACE;
 
@@ -292,6 +302,59 @@ kda_status kda_gate_chunk_cumsum(const kda_fwd_desc *d, const void *g, const flo
 
 // ---------------------------------------------------------------- backward
 namespace {
+
+// A second stream per device, created on first use, for work that overlaps the caller's
+// stream inside one call: the bf16 backward's operand preparation (which needs only the
+// forward's intermediates) beside the latency-bound recurrence, which occupies half the
+// CUs.  `ev` receives chunk_fwd_run's stage events, `done` marks the side work; `mu` is
+// held from the first event record to the caller stream's wait, so concurrent calls on
+// one device cannot interleave their records and waits.  Default stream priority.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kNumStages + 1] = {};
+    hipEvent_t done = nullptr;
+    std::mutex mu;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+hipError_t side_stream(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    std::lock_guard<std::mutex> lk(g_side_init);
+    if (!ss.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t ev[kNumStages + 2] = {};
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        for (int i = 0; i < kNumStages + 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) {  // nothing half-made is kept
+            for (hipEvent_t x : ev)
+                if (x) hipEventDestroy(x);
+            if (st) hipStreamDestroy(st);
+            return e;
+        }
+        for (int i = 0; i <= kNumStages; ++i) ss.ev[i] = ev[i];
+        ss.done = ev[kNumStages + 1];
+        ss.s = st;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
+// The side stream runs the operand preparation once the caller's stream has passed the
+// forward's intra stage (ss.ev[2], recorded by chunk_fwd_run before the recurrence); the
+// caller's stream then waits for it.
+hipError_t prep_beside_recurrence(SideStream &ss, const BwdChunkParams &P, hipStream_t stream) {
+    hipError_t e = hipStreamWaitEvent(ss.s, ss.ev[2], 0);
+    if (e == hipSuccess) e = launch_bwd_prep(P, ss.s);
+    if (e == hipSuccess) e = hipEventRecord(ss.done, ss.s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss.done, 0);
+    return e;
+}
 
 struct BwdLayout {
     size_t off_states, off_o, off_pdq, off_pdk, off_pdg, off_pdb, off_sstate, off_sw, off_da, off_tq, off_tk,
@@ -404,11 +467,22 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
     // backward steps 1-2: the forward with the state each chunk starts from (its output o
     // is not needed); its per-chunk intermediates stay in the workspace.  `saved`: a
     // kda_chunk_fwd_save call left them there already.
+    // bf16 chunked form: the operand preparation runs on the side stream beside the
+    // forward's recurrence.
+    const bool beside = chunked && p.qkv_bf16 && !saved && p.total_chunks > 0;
+    SideStream *ss = nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    if (beside) {
+        const hipError_t e = side_stream(&ss);
+        if (e != hipSuccess) return to_status(e);
+        side_lock = std::unique_lock<std::mutex>(ss->mu);
+    }
     if (!saved) {
         kda_fwd_desc fd = *d;
         fd.flags &= ~(uint32_t)KDA_OUTPUT_FINAL_STATE;
         st = chunk_fwd_run(&fd, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, ws + L.off_o, nullptr,
-                           true, states, workspace, FL.total_bytes, stream, nullptr, chunked && p.qkv_bf16, true);
+                           true, states, workspace, FL.total_bytes, stream, beside ? ss->ev : nullptr,
+                           chunked && p.qkv_bf16, true);
         if (st != KDA_OK) return st;
     }
 
@@ -456,6 +530,12 @@ kda_status bwd_run(const kda_fwd_desc *d, const void *q, const void *k, const vo
         P.rpack = reinterpret_cast<uint16_t *>(ws + L.off_rpack);
         P.ppack = reinterpret_cast<uint16_t *>(ws + L.off_ppack);
         P.doq = reinterpret_cast<uint16_t *>(ws + L.off_doq);
+    }
+    if (beside) {
+        const hipError_t e0 = prep_beside_recurrence(*ss, P, stream);
+        side_lock.unlock();
+        if (e0 != hipSuccess) return to_status(e0);
+        P.prep_done = 1;
     }
     hipError_t e = launch_bwd_dhu(P, stream);
     if (e == hipSuccess) e = launch_bwd_local(P, stream);

@@ -43,11 +43,14 @@ struct BwdChunkParams {
     uint16_t *ppack;                // Aqk^T [C][C], Qg^T [K][C] (permuted row fragments)
     uint16_t *doq;                  // dO [V][C] in accumulator-tile order
     float *cparam;                  // [total chunks * HV][K + 1] per-chunk dt_bias sums, then the A_log sum
+    int32_t prep_done;              // bf16: rpack, ppack and doq were written by launch_bwd_prep
+                                    // beforehand (else launch_bwd_dhu writes them first)
 };
 
 // The chunked backward covers K <= 128 (the token-level form above that).
 bool bwd_chunk_fits(int K);
 hipError_t launch_bwd_dhu(const BwdChunkParams &p, hipStream_t s);
+hipError_t launch_bwd_prep(const BwdChunkParams &p, hipStream_t s);  // bf16 only; else nothing
 hipError_t launch_bwd_local(const BwdChunkParams &p, hipStream_t s);
 hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_finish_chunked(const BwdChunkParams &p, hipStream_t s);

@@ -25,6 +25,26 @@ hipError_t launch_bwd_dhu_bf16(const BwdChunkParams &p, hipStream_t s) {
     }
     return hipErrorInvalidValue;
 }
+// the reverse recurrence's operand preparation alone (then not repeated by launch_bwd_dhu)
+hipError_t launch_bwd_prep_bf16(const BwdChunkParams &p, hipStream_t s) {
+    const int nkk = p.f.K / 32;
+    if (p.f.C == 64) {
+        switch (nkk) {
+        case 1: return launch_bwd_prep_t<64, 1>(p, s);
+        case 2: return launch_bwd_prep_t<64, 2>(p, s);
+        case 3: return launch_bwd_prep_t<64, 3>(p, s);
+        case 4: return launch_bwd_prep_t<64, 4>(p, s);
+        }
+    } else {
+        switch (nkk) {
+        case 1: return launch_bwd_prep_t<32, 1>(p, s);
+        case 2: return launch_bwd_prep_t<32, 2>(p, s);
+        case 3: return launch_bwd_prep_t<32, 3>(p, s);
+        case 4: return launch_bwd_prep_t<32, 4>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
 // the per-chunk gradients with every operand split into bf16 planes once (kda_bwd_local2.h)
 template <int C, int NKK>
 hipError_t launch_local2_t(const BwdChunkParams &p, hipStream_t s) {

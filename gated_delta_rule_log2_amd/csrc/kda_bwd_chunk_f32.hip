@@ -8,6 +8,10 @@ hipError_t launch_bwd_local_f32(const BwdChunkParams &p, hipStream_t s) { return
 bool bwd_chunk_fits(int K) { return K <= 128; }
 hipError_t launch_bwd_dhu_bf16(const BwdChunkParams &p, hipStream_t s);
 hipError_t launch_bwd_local_bf16(const BwdChunkParams &p, hipStream_t s);
+hipError_t launch_bwd_prep_bf16(const BwdChunkParams &p, hipStream_t s);
+hipError_t launch_bwd_prep(const BwdChunkParams &p, hipStream_t s) {
+    return p.f.qkv_bf16 ? launch_bwd_prep_bf16(p, s) : hipSuccess;
+}
 hipError_t launch_bwd_dhu(const BwdChunkParams &p, hipStream_t s) {
     return p.f.qkv_bf16 ? launch_bwd_dhu_bf16(p, s) : launch_bwd_dhu_f32(p, s);
 }

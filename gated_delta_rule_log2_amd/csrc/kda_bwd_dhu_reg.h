@@ -396,13 +396,17 @@ bwd_dhu_reg_kernel(BwdChunkParams P) {
 }
 
 template <int C, int NKK>
+hipError_t launch_bwd_prep_t(const BwdChunkParams &p, hipStream_t s) {
+    const unsigned slots = (unsigned)p.f.total_chunks * (unsigned)p.f.HV;
+    if (slots > 0) hipLaunchKernelGGL((bwd_prep_kernel<C, NKK>), dim3(slots), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int C, int NKK>
 hipError_t launch_bwd_dhu_reg_t(const BwdChunkParams &p, hipStream_t s) {
     constexpr int K = 32 * NKK;
-    const unsigned slots = (unsigned)p.f.total_chunks * (unsigned)p.f.HV;
-    if (slots > 0) {
-        auto prep = bwd_prep_kernel<C, NKK>;
-        hipLaunchKernelGGL(prep, dim3(slots), dim3(256), 0, s, p);
-        hipError_t e = hipGetLastError();
+    if (!p.prep_done) {
+        const hipError_t e = launch_bwd_prep_t<C, NKK>(p, s);
         if (e != hipSuccess) return e;
     }
     const int units = p.f.N * p.f.HV;

@@ -106,28 +106,6 @@ __device__ __forceinline__ void frag_rows_col(int f, int &row0, int &col) {
     col = HM ? 16 * j + lr : 8 * (lr >> 2) + 4 * j + (lr & 3);
 }
 
-// 4 x 4 transpose inside each quad of lanes (lanes 4a .. 4a + 3): lane 4a + q returns, as
-// its element i, element q of lane 4a + i.  Two exchange rounds (partner lane q ^ 1, then
-// q ^ 2), each moving the two elements whose index bit differs from the lane's bit.  The
-// recurrences hand over four consecutive rows of one column per lane, and the four lanes
-// of a quad hold four consecutive columns; after the transpose each lane holds four
-// consecutive columns of one row, so a [row][column] plane takes one 8-byte store per lane
-// and plane instead of four 2-byte ones.
-__device__ __forceinline__ float4 quad_transpose(float4 x) {
-    const int q = lane_id() & 3;
-    const bool q0 = (q & 1) != 0, q1 = (q & 2) != 0;
-    auto xor1 = [](float v) {  // quad_perm [1, 0, 3, 2]
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
-    };
-    auto xor2 = [](float v) {  // quad_perm [2, 3, 0, 1]
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
-    };
-    const float r0 = xor1(q0 ? x.x : x.y), r1 = xor1(q0 ? x.z : x.w);
-    const float t0 = q0 ? r0 : x.x, t1 = q0 ? x.y : r0, t2 = q0 ? r1 : x.z, t3 = q0 ? x.w : r1;
-    const float v0 = xor2(q1 ? t0 : t2), v1 = xor2(q1 ? t1 : t3);
-    return make_float4(q1 ? v0 : t0, q1 ? v1 : t1, q1 ? t2 : v0, q1 ? t3 : v1);
-}
-
 template <int C, int K>
 struct LocalLds2 {
     static constexpr int NB = C / 16, NPAIR = NB * (NB - 1) / 2, KH = K / 2;

@@ -231,6 +231,10 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_desc *d,
  * state gradients: 1.61 GB at B = 1, T = 8192, HV = 32, K = V = 128, bf16).  Errors: those of
  * kda_chunk_fwd, KDA_ERR_NULL_POINTER for a missing dout or required output when
  * B*T > 0.  Asynchronous on `stream`.  Results do not depend on scheduling (no atomics).
+ * With bf16 inputs and K <= 128 part of the work (the reverse recurrence's operand
+ * preparation) runs on a second stream of the library on the same device, created on the
+ * first call there, forked from and joined back into `stream` with events (so the call
+ * stays ordered on `stream`).
  */
 kda_status kda_chunk_bwd_workspace_size(const kda_fwd_desc *d, size_t *bytes);
 kda_status kda_chunk_bwd(const kda_fwd_desc *d,

@@ -20,6 +20,7 @@ hipError_t launch_recurrence(const Params &, hipStream_t) { ++g_stub_launches; r
 hipError_t launch_fused_recurrent(const Params &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_backward(const BwdParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_dhu(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
+hipError_t launch_bwd_prep(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_local(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_finish(const BwdParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
 hipError_t launch_bwd_finish_chunked(const BwdChunkParams &, hipStream_t) { ++g_stub_launches; return hipSuccess; }
