@@ -260,3 +260,51 @@ def test_saved_forward_backward_edges():
     saved_roundtrip(w, inp)
     w0 = GVA_BF16.replace(name="bwd_saved_T0", H=1, HV=2, K=64, V=64, T=0, h0="normal0.1")
     saved_roundtrip(w0)
+
+
+def test_backward_concurrent_streams_bitwise():
+    """Two host threads, each with its own stream and inputs, call the backward at the same
+    time (the bf16 chunked form shares the library's side stream of the device between
+    them); every gradient equals the one from a call made alone."""
+    import threading
+
+    cases = [GVA_BF16.replace(name="conc_a", T=300, H=1, HV=2, K=64, V=64, seed=21),
+             GVA_BF16.replace(name="conc_b", T=500, H=2, HV=4, K=128, V=64, seed=22)]
+    runs = []
+    for w in cases:
+        inp = make_inputs(w)
+        kw = kernel_kwargs(w)
+        kw.pop("output_final_state", None)
+        do, dht = cotangents(inp)
+        alone = gpu_grads(inp, kw, do, dht)
+        runs.append((inp, kw, do, dht, alone))
+    results = [[None] * 3 for _ in runs]
+    errors = []
+
+    def worker(j):
+        try:
+            inp, kw, do, dht, _ = runs[j]
+            d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for it in range(3):
+                    out = chunk_kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.to(DEV), dht=dht.to(DEV),
+                                        A_log=d["A_log"], dt_bias=d["dt_bias"], initial_state=d["initial_state"],
+                                        cu_seqlens=d["cu_seqlens"], **kw)
+                    results[j][it] = {k: v.clone() for k, v in out.items()}
+            s.synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(runs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for j, (_, _, _, _, alone) in enumerate(runs):
+        for it in range(3):
+            for key in alone:
+                assert torch.equal(results[j][it][key], alone[key]), f"{cases[j].name} call {it} {key} differs"
+    print("concurrent backward calls bit-identical", flush=True)
