@@ -322,13 +322,17 @@ __device__ __forceinline__ float4 ld4(const void *p, int64_t i, bool bf) {
     return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
 }
 
+// One row (token, qk head) per LANES lanes: a half wave when K <= 128 (every lane holds 4
+// elements), a whole wave for wider keys.
+template <int LANES>
 __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
-    const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-    if (row >= p.Ttot * p.H) return;  // whole waves only; no block barrier below
-    const int64_t t = row / p.H;
-    const int h = (int)(row % p.H), l = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / LANES) + (threadIdx.x / LANES);
+    const bool valid = row < p.Ttot * p.H;  // rows past the end still join the reductions
+    const int64_t t = valid ? row / p.H : 0;
+    const int h = valid ? (int)(row % p.H) : 0, l = threadIdx.x & (LANES - 1);
     const int group = p.HV / p.H, ns = p.nslices, K = p.K;
-    const bool on = 4 * l < K;
+    const bool on = valid && 4 * l < K;
+    auto rsum = [](float x) { return LANES == 32 ? half_sum(x) : wave_sum(x); };
     float4 gq = make_float4(0.f, 0.f, 0.f, 0.f), gk = gq, qv = gq, kv = gq;
     if (on) {
         for (int sl = 0; sl < ns; ++sl)
@@ -344,10 +348,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_qk_kernel(BwdParams p) {
     }
     float4 dq = make_float4(gq.x * p.scale, gq.y * p.scale, gq.z * p.scale, gq.w * p.scale), dk = gk;
     if (p.qk_l2norm) {
-        const float sq = wave_sum(qv.x * qv.x + qv.y * qv.y + qv.z * qv.z + qv.w * qv.w);
-        const float sk = wave_sum(kv.x * kv.x + kv.y * kv.y + kv.z * kv.z + kv.w * kv.w);
-        const float qd = wave_sum(qv.x * gq.x + qv.y * gq.y + qv.z * gq.z + qv.w * gq.w);
-        const float kd = wave_sum(kv.x * gk.x + kv.y * gk.y + kv.z * gk.z + kv.w * gk.w);
+        const float sq = rsum(qv.x * qv.x + qv.y * qv.y + qv.z * qv.z + qv.w * qv.w);
+        const float sk = rsum(kv.x * kv.x + kv.y * kv.y + kv.z * kv.z + kv.w * kv.w);
+        const float qd = rsum(qv.x * gq.x + qv.y * gq.y + qv.z * gq.z + qv.w * gq.w);
+        const float kd = rsum(kv.x * gk.x + kv.y * gk.y + kv.z * gk.z + kv.w * gk.w);
         const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
         // x^ = x r, r = (|x|^2 + eps)^-1/2:  dx = r dx^ - r^3 x (x . dx^)
         const float cq = rq * rq * rq * qd, ck = rk * rk * rk * kd;
@@ -483,7 +487,10 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t s) {
 // (activation chain rules), then the dt_bias and A_log token sums.
 hipError_t launch_bwd_finish(const BwdParams &p, hipStream_t s) {
     if (p.Ttot > 0) {
-        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
+        if (p.K <= 128)
+            hipLaunchKernelGGL(bwd_qk_kernel<32>, dim3((unsigned)((p.Ttot * p.H + 7) / 8)), dim3(kBwdThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL(bwd_qk_kernel<64>, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(p.Ttot * p.HV)), dim3(kBwdThreads), 0, s, p);
     }
     if (p.gate_mode != kGatePre) {
@@ -525,7 +532,10 @@ __global__ void __launch_bounds__(1024) bwd_chunk_param_kernel(BwdChunkParams P)
 hipError_t launch_bwd_finish_chunked(const BwdChunkParams &P, hipStream_t s) {
     const BwdParams &p = P.b;
     if (p.Ttot > 0)
-        hipLaunchKernelGGL(bwd_qk_kernel, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
+        if (p.K <= 128)
+            hipLaunchKernelGGL(bwd_qk_kernel<32>, dim3((unsigned)((p.Ttot * p.H + 7) / 8)), dim3(kBwdThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL(bwd_qk_kernel<64>, dim3((unsigned)((p.Ttot * p.H + 3) / 4)), dim3(kBwdThreads), 0, s, p);
     if (p.gate_mode != kGatePre && (p.ddt_bias || p.dA_log))
         hipLaunchKernelGGL(bwd_chunk_param_kernel, dim3((unsigned)p.HV), dim3(1024), 0, s, P);
     return hipGetLastError();
