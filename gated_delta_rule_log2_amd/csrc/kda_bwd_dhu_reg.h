@@ -43,34 +43,56 @@ struct DhuPack {
     static constexpr size_t pterm = (size_t)C * C + (size_t)K * C;  // Aqk^T [C][C], then Qg^T [K][C]
 };
 
-// Transposes one permuted-fragment bf16 matrix X [R][NC] into the permuted fragments
-// of X^T [NC][R] through LDS (buf: R rows of NC + 8).  CAUSAL: X is lower triangular
-// and its units right of the 16-row block's diagonal are zeros that were not written.
-template <bool CAUSAL>
-__device__ __forceinline__ void transpose_pfrag(const uint16_t *src, int R, int NC, uint16_t *dst, uint16_t *buf) {
-    const int ld = NC + 8;
-    const int nu = R * NC / 8;
-    for (int u = threadIdx.x; u < nu; u += blockDim.x) {
-        int row, col[8];
-        unit_coords<true>(u, NC, row, col);
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (!(CAUSAL && col[0] - col[0] % 32 > (row | 15))) x = *reinterpret_cast<const uint4 *>(src + (size_t)u * 8);
-        // elements 0..3 are columns col[0]..col[0]+3, elements 4..7 columns col[4]..col[4]+3
-        *reinterpret_cast<uint2 *>(buf + row * ld + col[0]) = make_uint2(x.x, x.y);
-        *reinterpret_cast<uint2 *>(buf + row * ld + col[4]) = make_uint2(x.z, x.w);
-    }
-    __syncthreads();
-    for (int u = threadIdx.x; u < nu; u += blockDim.x) {
-        int orow, ocol[8];
-        unit_coords<true>(u, R, orow, ocol);  // X^T has NC rows and R columns
-        uint32_t w[4];
+// Transposes one permuted-fragment bf16 matrix X [R][NC] into the permuted fragments of
+// X^T [NC][R] through LDS (buf: R rows of NC + 8), in two steps so that a workgroup can
+// request all of its matrices before staging the first: `load` brings this thread's units
+// into registers, `stage_store` writes them through LDS as X^T.  CAUSAL: X is lower
+// triangular and its units right of the 16-row block's diagonal are zeros that were not
+// written.
+template <int R, int NC, bool CAUSAL>
+struct PfragT {
+    static constexpr int NU = R * NC / 8, NPT = (NU + 255) / 256, LD = NC + 8;
+    static_assert(NU % 64 == 0, "whole waves");
+    __device__ static void load(const uint16_t *src, uint4 (&x)[NPT]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)buf[ocol[2 * e] * ld + orow] | ((uint32_t)buf[ocol[2 * e + 1] * ld + orow] << 16);
-        *reinterpret_cast<uint4 *>(dst + (size_t)u * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int k = 0; k < NPT; ++k) {
+            const int u = (int)threadIdx.x + 256 * k;
+            x[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < NU) {
+                int row, col[8];
+                unit_coords<true>(u, NC, row, col);
+                if (!(CAUSAL && col[0] - col[0] % 32 > (row | 15))) x[k] = *reinterpret_cast<const uint4 *>(src + (size_t)u * 8);
+            }
+        }
     }
-    __syncthreads();
-}
+    __device__ static void stage_store(const uint4 (&x)[NPT], uint16_t *buf, uint16_t *dst) {
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int u = (int)threadIdx.x + 256 * k;
+            if (u < NU) {
+                int row, col[8];
+                unit_coords<true>(u, NC, row, col);
+                *reinterpret_cast<uint2 *>(buf + row * LD + col[0]) = make_uint2(x[k].x, x[k].y);
+                *reinterpret_cast<uint2 *>(buf + row * LD + col[4]) = make_uint2(x[k].z, x[k].w);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int u = (int)threadIdx.x + 256 * k;
+            if (u < NU) {
+                int orow, ocol[8];
+                unit_coords<true>(u, R, orow, ocol);  // X^T has NC rows and R columns
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (uint32_t)buf[ocol[2 * e] * LD + orow] | ((uint32_t)buf[ocol[2 * e + 1] * LD + orow] << 16);
+                *reinterpret_cast<uint4 *>(dst + (size_t)u * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        __syncthreads();
+    }
+};
 
 // One workgroup of 256 threads per (chunk, value head) slot.
 template <int C, int NKK>
@@ -87,10 +109,19 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdChunkParams P) {
     const uint16_t *W = static_cast<const uint16_t *>(p.w_W) + slot * C * K;
     const uint16_t *KgT = static_cast<const uint16_t *>(p.w_KgT) + slot * K * C;
     uint16_t *ring = P.rpack + slot * PK::ring, *pterm = P.ppack + slot * PK::pterm;
-    transpose_pfrag<false>(KgT, K, C, ring, buf);                 // Kg     [C][K]
-    transpose_pfrag<false>(W, C, K, ring + (size_t)C * K, buf);   // W^T    [K][C]
-    transpose_pfrag<true>(Aqk, C, C, pterm, buf);                 // Aqk^T  [C][C]
-    transpose_pfrag<false>(Qg, C, K, pterm + (size_t)C * C, buf); // Qg^T   [K][C]
+    // all four matrices requested before the first is staged
+    using TK = PfragT<K, C, false>;
+    using TW = PfragT<C, K, false>;
+    using TA = PfragT<C, C, true>;
+    uint4 xk[TK::NPT], xw[TW::NPT], xa[TA::NPT], xq[TW::NPT];
+    TK::load(KgT, xk);
+    TW::load(W, xw);
+    TA::load(Aqk, xa);
+    TW::load(Qg, xq);
+    TK::stage_store(xk, buf, ring);                      // Kg     [C][K]
+    TW::stage_store(xw, buf, ring + (size_t)C * K);      // W^T    [K][C]
+    TA::stage_store(xa, buf, pterm);                     // Aqk^T  [C][C]
+    TW::stage_store(xq, buf, pterm + (size_t)C * C);     // Qg^T   [K][C]
     // dO of the chunk in accumulator-tile order (see quad_off), rows past the end zero
     const ChunkInfo ci = chunk_info(p, gc);
     const int V = p.V;
